@@ -1,0 +1,179 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Function names follow include/moe.h.  Device buffers are torch tensors on the
+current HIP device; the stream is torch's current stream.  Nothing here
+computes any part of the layer: every step runs in the library.  If the
+library is missing the import fails loudly -- there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EFORMAT, MOE_EWORKSPACE, MOE_EDEVICE, MOE_ECODE = 0, -1, -2, -3, -4, -5, -6
+FMT = {"TERN160": 1, "Q2_0": 2, "Q3": 3, "MXFP4": 4, "Q8": 5}
+FMT_NAME = {v: k for k, v in FMT.items()}
+MAX_DECODE_ROWS = 8
+MAX_TOP_K = 8
+
+# every symbol include/moe.h declares
+EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
+           "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
+           "moe_layer", "moe_layer_profiled")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn}: {status} ({status_string(status)})")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+class ExpertRef(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("gate", ctypes.c_uint64), ("up", ctypes.c_uint64), ("down", ctypes.c_uint64)]
+
+
+EXPERT_REF_DTYPE = np.dtype([("fmt", "<u4"), ("reserved", "<u4"), ("gate", "<u8"),
+                             ("up", "<u8"), ("down", "<u8")])
+assert EXPERT_REF_DTYPE.itemsize == ctypes.sizeof(ExpertRef) == 32
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m bit_moe_expert_02_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        dims_p = ctypes.POINTER(Dims)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_packed_bytes.restype = sz
+        L.moe_packed_bytes.argtypes = [ctypes.c_int, i64, i64]
+        L.moe_pack.restype = ctypes.c_int
+        L.moe_pack.argtypes = [ctypes.c_int, vp, i64, i64, vp, sz, ctypes.c_int]
+        L.moe_unpack.restype = ctypes.c_int
+        L.moe_unpack.argtypes = [ctypes.c_int, vp, sz, i64, i64, vp, ctypes.c_int]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [dims_p, i32]
+        L.moe_check_experts.restype = ctypes.c_int
+        L.moe_check_experts.argtypes = [dims_p, vp, i32, sz]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_route.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_expert_ffn.restype = ctypes.c_int
+        L.moe_expert_ffn.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer.restype = ctypes.c_int
+        L.moe_layer.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_profiled.restype = ctypes.c_int
+        L.moe_layer_profiled.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         vp, vp, i32]
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(fn, st):
+    if st != MOE_OK:
+        raise MoeError(fn, st)
+
+
+# ----------------------------------------------------------------------------- host packer
+def packed_bytes(fmt, n, k):
+    return int(lib().moe_packed_bytes(FMT[fmt], int(n), int(k)))
+
+
+def pack(fmt, w, nthreads=0):
+    """fp32 [n, k] (numpy) -> packed uint8 array (numpy), via moe_pack."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    nbytes = packed_bytes(fmt, n, k)
+    if nbytes == 0:
+        raise MoeError("moe_packed_bytes", MOE_ESHAPE)
+    out = np.empty(nbytes, np.uint8)
+    _check("moe_pack", lib().moe_pack(FMT[fmt], w.ctypes.data, n, k, out.ctypes.data, nbytes,
+                                      int(nthreads)))
+    return out
+
+
+def pack_into(fmt, w, out, nthreads=0):
+    """Packs into a preallocated uint8 numpy array view (for large buffers)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    _check("moe_pack", lib().moe_pack(FMT[fmt], w.ctypes.data, n, k, out.ctypes.data, out.size,
+                                      int(nthreads)))
+
+
+def unpack(fmt, buf, n, k, nthreads=0):
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    out = np.empty((n, k), np.float32)
+    _check("moe_unpack", lib().moe_unpack(FMT[fmt], buf.ctypes.data, buf.size, int(n), int(k),
+                                          out.ctypes.data, int(nthreads)))
+    return out
+
+
+# ----------------------------------------------------------------------------- device calls
+def dims(hidden, inter, n_experts, top_k):
+    return Dims(hidden, inter, n_experts, top_k)
+
+
+def workspace_bytes(d, rows):
+    return int(lib().moe_workspace_bytes(ctypes.byref(d), int(rows)))
+
+
+def check_experts(d, table, weights_bytes):
+    table = np.ascontiguousarray(table, dtype=EXPERT_REF_DTYPE)
+    return int(lib().moe_check_experts(ctypes.byref(d), table.ctypes.data, len(table),
+                                       int(weights_bytes)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_route(d, x, rows, w_router, bias, idx, wts, ws, stream=None):
+    _check("moe_route", lib().moe_route(ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router),
+                                        _ptr(bias), _ptr(idx), _ptr(wts), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_expert_ffn(d, x, rows, idx, wts, weights, experts, shared, y, ws, stream=None):
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        ctypes.byref(d), _ptr(x), int(rows), _ptr(idx), _ptr(wts), _ptr(weights), _ptr(experts),
+        _ptr(shared), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer(d, x, rows, w_router, bias, weights, experts, shared, idx, wts, y, ws, stream=None):
+    _check("moe_layer", lib().moe_layer(
+        ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router), _ptr(bias), _ptr(weights),
+        _ptr(experts), _ptr(shared), _ptr(idx), _ptr(wts), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_profiled(d, x, rows, w_router, bias, weights, experts, shared, idx, wts, y, ws,
+                       events, stream=None):
+    arr = (ctypes.c_void_p * len(events))(*events)
+    _check("moe_layer_profiled", lib().moe_layer_profiled(
+        ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router), _ptr(bias), _ptr(weights),
+        _ptr(experts), _ptr(shared), _ptr(idx), _ptr(wts), _ptr(y), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream), arr, len(events)))

@@ -1,0 +1,127 @@
+"""Device-resident MoE layers: packing with the library's packer, placement in
+one HBM buffer, the expert table, and thin calls into the C ABI.
+
+Layout of a layer's weight buffer: every expert's gate, up and down matrices
+(planar packed, include/moe.h) back to back, each starting on a 256-byte
+boundary; the shared expert last.  The expert table (one 32-byte record per
+routed expert) lives in device memory beside it.
+"""
+
+import numpy as np
+
+from . import _lib as L
+from . import synth
+
+ALIGN = 256
+
+
+def _align(v):
+    return (v + ALIGN - 1) // ALIGN * ALIGN
+
+
+def expert_sizes(fmt, hidden, inter):
+    gu = L.packed_bytes(fmt, inter, hidden)
+    dn = L.packed_bytes(fmt, hidden, inter)
+    return gu, dn
+
+
+def plan(fmts, shared_fmt, hidden, inter):
+    """Byte offsets of each expert's matrices; returns (table, shared_ref, total)."""
+    table = np.zeros(len(fmts), L.EXPERT_REF_DTYPE)
+    off = 0
+    for e, f in enumerate(fmts):
+        gu, dn = expert_sizes(f, hidden, inter)
+        table[e] = (L.FMT[f], 0, off, _align(off + gu), _align(_align(off + gu) + gu))
+        off = _align(table[e]["down"] + dn)
+    shared = None
+    if shared_fmt is not None:
+        gu, dn = expert_sizes(shared_fmt, hidden, inter)
+        shared = np.zeros(1, L.EXPERT_REF_DTYPE)
+        shared[0] = (L.FMT[shared_fmt], 0, off, _align(off + gu), _align(_align(off + gu) + gu))
+        off = _align(shared[0]["down"] + dn)
+    return table, shared, off
+
+
+class DeviceLayer:
+    """One MoE layer of a workload, resident on the current HIP device.
+
+    materialize: iterable of routed expert ids whose weights are generated and
+    packed; every other slot is zero-filled (an all-zero expert in every
+    format), or filled from `pool` when given.
+    pool: dict fmt -> list of packed expert triples (gate, up, down) as numpy
+    uint8 arrays; slot e takes pool[fmt][e % len(pool[fmt])].
+    """
+
+    def __init__(self, wl, layer, materialize=(), pool=None, device="cuda"):
+        import torch
+        self.wl, self.layer = wl, layer
+        self.dims = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k)
+        self.fmts = synth.format_map(wl, layer)
+        table, shared, total = plan(self.fmts, wl.shared_fmt, wl.hidden, wl.inter)
+        self.table, self.shared_table, self.total = table, shared, total
+        st = L.check_experts(self.dims, table, total)
+        if st != L.MOE_OK:
+            raise L.MoeError("moe_check_experts", st)
+        self.weights = torch.zeros(total, dtype=torch.uint8, device=device)
+        self.materialized = set()
+        for e in sorted(set(int(v) for v in materialize)):
+            self._put(e, *self.pack_expert(e))
+            self.materialized.add(e)
+        if pool is not None:
+            for e in range(wl.n_experts):
+                if e not in self.materialized:
+                    p = pool[self.fmts[e]]
+                    self._put_dev(e, p[e % len(p)])
+        if wl.shared_fmt is not None:
+            self._put(-1, *self.pack_expert(wl.n_experts))
+        self.experts = torch.from_numpy(table.view(np.uint8).copy()).to(device)
+        self.shared = (torch.from_numpy(shared.view(np.uint8).copy()).to(device)
+                       if shared is not None else None)
+        self.router = torch.from_numpy(synth.router(wl, layer)).to(device)
+        b = synth.bias(wl, layer)
+        self.bias = torch.from_numpy(b).to(device) if b is not None else None
+
+    def fmt_of(self, e):
+        return self.wl.shared_fmt if e < 0 or e == self.wl.n_experts else self.fmts[e]
+
+    def pack_expert(self, e):
+        """Generate expert e (n_experts = the shared one) and pack it with moe_pack."""
+        fmt = self.wl.shared_fmt if e == self.wl.n_experts else self.fmts[e]
+        g, u, d = synth.expert_weights(self.wl, self.layer, e)
+        return L.pack(fmt, g), L.pack(fmt, u), L.pack(fmt, d)
+
+    def _ref(self, e):
+        return self.shared_table[0] if e < 0 else self.table[e]
+
+    def _put(self, e, g, u, d):
+        import torch
+        ref = self._ref(e)
+        for off, buf in ((ref["gate"], g), (ref["up"], u), (ref["down"], d)):
+            self.weights[int(off):int(off) + buf.size].copy_(torch.from_numpy(buf))
+
+    def _put_dev(self, e, triple):
+        ref = self._ref(e)
+        for off, buf in zip((ref["gate"], ref["up"], ref["down"]), triple):
+            self.weights[int(off):int(off) + buf.numel()].copy_(buf)
+
+
+def make_pool(wl, layer, fmts, count, device="cuda"):
+    """Distinct packed experts per format (device tensors), for throughput-only slots."""
+    import torch
+    pool = {}
+    for f in sorted(set(fmts)):
+        items = []
+        for i in range(count):
+            g, u, d = synth.expert_weights(wl, layer + 1000 * (1 + list(L.FMT).index(f)), i)
+            items.append(tuple(torch.from_numpy(L.pack(f, m)).to(device) for m in (g, u, d)))
+        pool[f] = items
+    return pool
+
+
+def workspace(d, rows, device="cuda"):
+    """A zero-filled workspace of moe_workspace_bytes(d, rows)."""
+    import torch
+    n = L.workspace_bytes(d, rows)
+    if n == 0:
+        raise L.MoeError("moe_workspace_bytes", L.MOE_ESHAPE)
+    return torch.zeros(n, dtype=torch.uint8, device=device)

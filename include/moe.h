@@ -1,0 +1,212 @@
+/*
+ * moe.h -- C ABI of libmoe: a low-bit routed-MoE expert FFN for one AMD
+ * MI355X (gfx950).
+ *
+ * The computation (sources cited by page title and section):
+ *   - "DeepSeek-V4.1-Flash served three ways on 4xL20" (lcz.me/topic/2356),
+ *     section 1: the decoder layer -- hidden 5120, moe_intermediate 2304,
+ *     384 routed experts, top-6, one shared expert; section 2: an expert is
+ *     three 5120x2304 matrices and decode cost is the expert bytes a token
+ *     selects.
+ *   - "[Strata] DeepSeek V4.1 Flash on a single 4090" (lcz.me/post/25274),
+ *     section 5.1: per-expert mixed low-bit formats (ternary, Q2_0, Q3);
+ *     section 5.3: a selection-only route bias that leaves mixing weights exact;
+ *     section 2: the int8 (Q8_0) dense half.
+ *
+ * Per layer and per row r of x:
+ *     logits[r,e] = sum_h x[r,h] * Wr[e,h]                 (router GEMV, fp64 sums)
+ *     S_r         = the top_k experts by logits[r,e] + bias[e],
+ *                   ties toward the lower expert id, ordered by key desc
+ *     w[r,e]      = softmax over S_r of the UNBIASED logits
+ *     y[r]        = sum_{e in S_r, ascending e} w[r,e] * FFN_e(x[r]) + FFN_shared(x[r])
+ *     FFN(x)      = W_down (silu(W_gate x) * (W_up x)),  silu(z) = z / (1 + e^-z)
+ *
+ * Weight formats (block layouts are this library's definitions; the pages
+ * give the formats' names and bit rates only):
+ *   MOE_FMT_Q2_0    64 w/block: 16 code bytes (weight i = bits [2i,2i+2) of the
+ *                   128-bit LE code word) + fp16 d;  value d*(c-2).     2.25 bpw
+ *   MOE_FMT_TERN160 160 w/block: 32 bytes, byte j = sum_m (t_{5j+m}+1)*3^m
+ *                   (values 243..255 invalid) + fp16 d; value d*t.  Rows whose
+ *                   length is not a multiple of 160 are padded with zero trits.
+ *   MOE_FMT_Q3      256 w/block, 16 sub-blocks of 16: 64-byte low plane (low 2
+ *                   bits of q_i at bits [2i,2i+2)), 32-byte high plane (32-bit
+ *                   word m: bit 2i = high bit of weight i of sub-block 2m, bit
+ *                   2i+1 = of sub-block 2m+1), fp16 d, 12 bytes of sixteen 6-bit
+ *                   u_j at bits [6j,6j+6);  value d*(u_j-32)*(q-4).  3.4375 bpw
+ *   MOE_FMT_MXFP4   32 w/block: 16 bytes of e2m1 (element i in byte i/2, low
+ *                   nibble for even i) + e8m0 E (255 invalid);
+ *                   value 2^(E-127)*e2m1 (OCP MX v1.0).                 4.25 bpw
+ *   MOE_FMT_Q8      32 w/block: 32 int8 + fp16 d; value d*q.           8.5 bpw
+ * Every matrix W[N x K] is planar: codes of all blocks in (row, block) order,
+ * then the scales in the same order (Q3: all fp16 d, then all 12-byte u records).
+ *
+ * Conventions for every entry point:
+ *   - Return value: MOE_OK (0) or a negative moe_status.  Argument, shape and
+ *     format errors are detected on the host before anything is launched.
+ *   - Device pointers are HIP device (or managed) memory on the current device.
+ *     The caller owns every buffer; the library never allocates or frees.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
+ *     asynchronous on it; nothing synchronises the host.  Device faults surface
+ *     at the caller's next synchronisation.
+ *   - The library keeps no mutable global state: calls on different streams
+ *     with different workspaces may run concurrently.
+ */
+#ifndef BIT_MOE_H
+#define BIT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,      /* null pointer, negative size, bad flag            */
+  MOE_ESHAPE = -2,      /* dims the kernels do not support / K not a block multiple */
+  MOE_EFORMAT = -3,     /* unknown format tag                                */
+  MOE_EWORKSPACE = -4,  /* workspace smaller than moe_workspace_bytes()      */
+  MOE_EDEVICE = -5,     /* a HIP launch or runtime call failed               */
+  MOE_ECODE = -6        /* moe_unpack met an invalid code (ternary byte > 242, e8m0 255) */
+} moe_status;
+
+typedef enum {
+  MOE_FMT_TERN160 = 1,
+  MOE_FMT_Q2_0 = 2,
+  MOE_FMT_Q3 = 3,
+  MOE_FMT_MXFP4 = 4,
+  MOE_FMT_Q8 = 5
+} moe_format;
+
+/* Largest number of rows the decode kernels take in one call (one token or
+ * one speculative-verify window of up to 8 candidates). */
+#define MOE_MAX_DECODE_ROWS 8
+/* Largest top_k the selection kernel takes. */
+#define MOE_MAX_TOP_K 8
+
+const char* moe_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side packer.  Pure functions of their arguments, thread-safe, touch  */
+/* no device.                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of one packed N x K matrix in `fmt`: N * ceil(K/B) * (code + scale
+ * bytes).  Returns 0 for an unknown format, n <= 0, k <= 0, or (except
+ * TERN160) K not a multiple of the block size. */
+size_t moe_packed_bytes(int fmt, int64_t n, int64_t k);
+
+/* Round-to-nearest packing of a row-major fp32 matrix w[n x k] (host memory)
+ * into dst (host, dst_bytes >= moe_packed_bytes).  Arithmetic is IEEE fp32
+ * with ties to even; fp16 scales round to nearest even and saturate at
+ * +-65504.  Per-format rules:
+ *   Q2_0    m = block element of largest |w| (first on ties), d = fp16(m/-2),
+ *           c = clamp(rint(w/d)+2, 0, 3)           (d == 0: c = 2)
+ *   TERN160 d = fp16(max|w|), t = clamp(rint(w/d), -1, 1)   (d == 0: t = 0)
+ *   Q3      sigma_j = m_j/-4 per sub-block, d = fp16(max|sigma_j|/31),
+ *           u_j = clamp(rint(sigma_j/d), -31, 31) + 32,
+ *           q = clamp(rint(w/(d*(u_j-32))) + 4, 0, 7)  (zero divisor: u=32, q=4)
+ *   MXFP4   E = clamp(floor(log2 amax) - 2 + 127, 0, 254) (amax 0: E 0),
+ *           element = e2m1 nearest-even of w/2^(E-127), saturating at 6;
+ *           the sign bit is the sign bit of w
+ *   Q8      d = fp16(max|w|/127), q = clamp(rint(w/d), -127, 127)
+ * nthreads <= 0 uses the hardware concurrency.  Non-finite inputs give
+ * unspecified (but valid) codes. */
+int moe_pack(int fmt, const float* w, int64_t n, int64_t k, void* dst, size_t dst_bytes,
+             int nthreads);
+
+/* Exact decode of a packed matrix (host) to fp32 w[n x k] (host).  TERN160
+ * padding columns are dropped.  Returns MOE_ECODE on an invalid code.
+ * Every decoded value is exact in fp32, except MXFP4 values of magnitude
+ * 2^128 and above (E = 254 with |e2m1| >= 2), which decode to +-inf. */
+int moe_unpack(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k, float* w,
+               int nthreads);
+
+/* ------------------------------------------------------------------------ */
+/* Device layer.                                                             */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t hidden;     /* H: 5120 for the real layer, 512 for the tiny one       */
+  int32_t inter;      /* I: 2304 / 256                                          */
+  int32_t n_experts;  /* E routed experts: 384 / 16                             */
+  int32_t top_k;      /* k: 6 / 2                                               */
+} moe_dims;
+
+/* One expert: its format and the byte offsets of its three packed matrices
+ * inside the `weights` buffer: gate [I x H], up [I x H], down [H x I].  Each
+ * offset must be a multiple of 16. */
+typedef struct {
+  uint32_t fmt;
+  uint32_t reserved;  /* must be 0 */
+  uint64_t gate, up, down;
+} moe_expert_ref;
+
+/* Supported shapes: (hidden, inter) = (5120, 2304) or (512, 256);
+ * 1 <= top_k <= MOE_MAX_TOP_K, top_k <= n_experts <= 4096,
+ * rows * top_k <= 64, rows <= MOE_MAX_DECODE_ROWS.  Returns 0 for
+ * unsupported dims. */
+size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows);
+
+/* Host check of an expert table (host memory) against the dims and the size
+ * of the weights buffer: format tags, reserved fields, alignment, and that
+ * every matrix lies inside [0, weights_bytes).  The device entry points read
+ * the table from device memory and trust it; validate it once with this call
+ * before uploading. */
+int moe_check_experts(const moe_dims* dims, const moe_expert_ref* table, int32_t count,
+                      size_t weights_bytes);
+
+/* Router GEMV + selection.
+ *   x_bf16   [rows x H] bf16, device
+ *   w_router [E x H] fp32, device
+ *   sel_bias [E] fp32, device, or NULL (no bias).  Changes selection only.
+ *   idx      [rows x top_k] int32, device, out: selected ids, key desc / id asc
+ *   wts      [rows x top_k] fp32, device, out: mixing weights (unbiased softmax
+ *            renormalised over the selection)
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(dims, rows).
+ *            It must be zero-filled before its first use; every call leaves it
+ *            ready for the next.  One workspace must not serve two calls that
+ *            can overlap.
+ * rows == 0 returns MOE_OK and launches nothing. */
+int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
+              const float* sel_bias, int32_t* idx, float* wts, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* Grouped expert FFN for a given routing.
+ *   idx, wts   [rows x top_k], device, as produced by moe_route (any order of
+ *              the k entries of a row is accepted; each row's ids must be
+ *              distinct and < n_experts)
+ *   weights    device buffer holding every packed matrix
+ *   experts    [n_experts] moe_expert_ref, device
+ *   shared     [1] moe_expert_ref, device, or NULL (no shared expert)
+ *   y          [rows x H] fp32, device, out (overwritten)
+ * Deterministic: the same inputs give bitwise the same y. */
+int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const int32_t* idx,
+                   const float* wts, const void* weights, const moe_expert_ref* experts,
+                   const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* The whole layer: moe_route followed by moe_expert_ffn, with the shared
+ * expert's gate/up streamed concurrently with the router.  idx and wts are
+ * outputs as in moe_route. */
+int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
+              const float* sel_bias, const void* weights, const moe_expert_ref* experts,
+              const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* moe_layer with timing: `events` holds n_events >= 4 hipEvent_t handles
+ * created by the caller.  events[0] is recorded before the first kernel and
+ * events[i] after the i-th of the layer's three kernels (router + shared
+ * gate/up, routed gate/up, down + combine). */
+int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
+                       const float* w_router, const float* sel_bias, const void* weights,
+                       const moe_expert_ref* experts, const moe_expert_ref* shared,
+                       int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes,
+                       void* stream, void* const* events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BIT_MOE_H */

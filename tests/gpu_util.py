@@ -1,0 +1,75 @@
+"""Helpers for the GPU parity tests: oracle references built from the seeded
+inputs, device layers built with the library's packer, and comparisons.
+
+The oracle never sees anything the HIP path produced: it packs and decodes the
+same seeded fp32 weights with its own code, and routes the same bf16 x."""
+
+import numpy as np
+
+from bit_moe_expert_02_amd import _lib as L
+from bit_moe_expert_02_amd import layer as LY
+from bit_moe_expert_02_amd import synth
+from oracle import formats as OF
+from oracle import moe as OM
+
+REL_L2_TOL = 1e-3     # per row, against the fp64 oracle
+W_RTOL = 1e-6         # mixing weights (fp32 on the device)
+NEAR_TIE = 1e-9       # relative key gap below which an index mismatch would be a tie
+
+
+def oracle_expert(wl, layer, e):
+    """Decoded fp64 (gate, up, down) of routed expert e, or the shared one (e == n_experts)."""
+    fmt = wl.shared_fmt if e == wl.n_experts else synth.format_map(wl, layer)[e]
+    g, u, d = synth.expert_weights(wl, layer, e)
+    return (OF.decode(fmt, OF.pack(fmt, g), wl.inter, wl.hidden),
+            OF.decode(fmt, OF.pack(fmt, u), wl.inter, wl.hidden),
+            OF.decode(fmt, OF.pack(fmt, d), wl.hidden, wl.inter))
+
+
+def oracle_route(wl, layer, xbits):
+    x = OM.bf16_to_f64(xbits)
+    idx, w, logits, gap = OM.route(x, synth.router(wl, layer), wl.top_k, synth.bias(wl, layer))
+    return x, idx, w, logits, gap
+
+
+def oracle_y(wl, layer, x, idx, w, rows):
+    """Oracle y for the given rows (list of row numbers)."""
+    cache = {}
+
+    def ex(e):
+        if e not in cache:
+            cache[e] = oracle_expert(wl, layer, e)
+        return cache[e]
+
+    shared = ex(wl.n_experts) if wl.shared_fmt is not None else None
+    return OM.combine(x[rows], idx[rows], w[rows], ex, shared)
+
+
+def rel_l2_rows(got, ref):
+    got = np.asarray(got, np.float64)
+    return np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)
+
+
+def device_inputs(wl, layer, xbits):
+    import torch
+    x = torch.from_numpy(xbits.view(np.int16).copy()).cuda()
+    return x
+
+
+def run_layer(dl, x, rows):
+    import torch
+    ws = LY.workspace(dl.dims, rows)
+    idx = torch.zeros((rows, dl.wl.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((rows, dl.wl.top_k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((rows, dl.wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_layer(dl.dims, x, rows, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
+                idx, wts, y, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), wts.cpu().numpy(), y.cpu().numpy(), ws
+
+
+def check_routing(idx_gpu, w_gpu, idx_ref, w_ref, gap, logits):
+    scale = np.max(np.abs(logits), axis=1)
+    assert np.all(gap > NEAR_TIE * scale), "near-tie in the selection keys: inputs are ambiguous"
+    assert np.array_equal(idx_gpu, idx_ref)
+    np.testing.assert_allclose(w_gpu, w_ref, rtol=W_RTOL, atol=0)

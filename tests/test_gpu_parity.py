@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar: expert indices bit-exact; mixing weights within 1e-6 relative; layer
+output within 1e-3 relative L2 per row.  Real-shape layers materialise only
+the experts the checked rows select (every other slot is an all-zero expert;
+a wrong selection would therefore also show up in y)."""
+
+import numpy as np
+import pytest
+
+from tests import gpu_util as G
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from bit_moe_expert_02_amd import _lib as L          # noqa: E402
+from bit_moe_expert_02_amd import layer as LY        # noqa: E402
+from bit_moe_expert_02_amd import synth              # noqa: E402
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    L.lib()
+
+
+# ------------------------------------------------------------------ tiny layer
+@pytest.mark.parametrize("rows,stream", [(4, 0), (1, 1), (2, 2), (5, 3), (8, 4)])
+def test_tiny_layer(rows, stream):
+    wl = synth.WORKLOADS["tiny"]
+    _say("tiny layer rows", rows, "x stream", stream)
+    xbits = synth.x_bf16(wl, 0, rows, stream)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
+    gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), rows)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    ref = G.oracle_y(wl, 0, x, idx, w, list(range(rows)))
+    err = G.rel_l2_rows(gy, ref)
+    _say("  rel L2 per row", err)
+    assert np.all(err <= G.REL_L2_TOL)
+
+
+def test_tiny_repeated_rows_share_experts():
+    """Identical rows select identical experts: each expert serves 5 rows
+    (more than one staging batch)."""
+    wl = synth.WORKLOADS["tiny"]
+    xbits = np.repeat(synth.x_bf16(wl, 0, 1, 7), 5, axis=0)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
+    gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), 5)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    ref = G.oracle_y(wl, 0, x, idx, w, list(range(5)))
+    assert np.all(G.rel_l2_rows(gy, ref) <= G.REL_L2_TOL)
+    assert np.array_equal(gy[0], gy[4])
+
+
+def test_tiny_deterministic_and_workspace_reuse():
+    wl = synth.WORKLOADS["tiny"]
+    dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
+    ys = []
+    ws = LY.workspace(dl.dims, 8)
+    for rep, stream in enumerate([10, 11, 10]):
+        xbits = synth.x_bf16(wl, 0, 8, stream)
+        xd = G.device_inputs(wl, 0, xbits)
+        idx = torch.zeros((8, 2), dtype=torch.int32, device="cuda")
+        wts = torch.zeros((8, 2), dtype=torch.float32, device="cuda")
+        y = torch.zeros((8, wl.hidden), dtype=torch.float32, device="cuda")
+        L.moe_layer(dl.dims, xd, 8, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
+                    idx, wts, y, ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+        x, ri, rw, logits, gap = G.oracle_route(wl, 0, xbits)
+        assert np.array_equal(idx.cpu().numpy(), ri)
+        assert np.all(G.rel_l2_rows(ys[-1], G.oracle_y(wl, 0, x, ri, rw, list(range(8)))) <= G.REL_L2_TOL)
+    assert np.array_equal(ys[0], ys[2])            # bitwise reproducible
+    # the workspace's counters are back at zero after every call
+    assert not torch.any(ws[: 4 * 1025].view(torch.int32)).item()
+
+
+def test_route_only_and_ffn_only_match_layer():
+    wl = synth.WORKLOADS["tiny"]
+    dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
+    xbits = synth.x_bf16(wl, 0, 3, 5)
+    xd = G.device_inputs(wl, 0, xbits)
+    ws = LY.workspace(dl.dims, 3)
+    idx = torch.zeros((3, 2), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((3, 2), dtype=torch.float32, device="cuda")
+    L.moe_route(dl.dims, xd, 3, dl.router, dl.bias, idx, wts, ws)
+    y = torch.zeros((3, wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_expert_ffn(dl.dims, xd, 3, idx, wts, dl.weights, dl.experts, dl.shared, y, ws)
+    torch.cuda.synchronize()
+    gi, gw, gy, _ = G.run_layer(dl, xd, 3)
+    assert np.array_equal(idx.cpu().numpy(), gi)
+    assert np.array_equal(wts.cpu().numpy(), gw)
+    np.testing.assert_allclose(y.cpu().numpy(), gy, rtol=1e-6, atol=1e-7)
+
+
+def test_tiny_topk_max():
+    """top_k = 8 of 16 (the largest the selection kernel takes), no shared expert."""
+    base = synth.WORKLOADS["tiny"]
+    wl = synth.Workload("tiny_k8", 11, 512, 256, 16, 8, "Q2_0", None, rows=(2,))
+    xbits = synth.x_bf16(wl, 0, 8, 0)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    dl = LY.DeviceLayer(wl, 0, materialize=range(16))
+    gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), 8)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    assert np.all(G.rel_l2_rows(gy, G.oracle_y(wl, 0, x, idx, w, list(range(8)))) <= G.REL_L2_TOL)
+    del base
+
+
+# ------------------------------------------------------------------ real shapes
+def _real_case(wl, rows, stream, check_rows):
+    xbits = synth.x_bf16(wl, 0, rows, stream)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    need = sorted(set(idx[check_rows].reshape(-1).tolist()))
+    _say(f"{wl.name}: rows {rows}, checking rows {check_rows}, experts {need}")
+    dl = LY.DeviceLayer(wl, 0, materialize=need)
+    gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), rows)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    ref = G.oracle_y(wl, 0, x, idx, w, check_rows)
+    err = G.rel_l2_rows(gy[check_rows], ref)
+    _say("  rel L2 per checked row", err)
+    assert np.all(err <= G.REL_L2_TOL)
+    return gy
+
+
+def test_decode_q2_layer_one_row():
+    _real_case(synth.WORKLOADS["decode_q2"], 1, 0, [0])
+
+
+@pytest.mark.parametrize("rows,check", [(1, [0]), (5, [2]), (8, [0, 7])])
+def test_mixed_verify_layer(rows, check):
+    _real_case(synth.WORKLOADS["mixed_verify"], rows, rows, check)
+
+
+@pytest.mark.parametrize("fmt", ["TERN160", "Q2_0", "Q3", "MXFP4", "Q8"])
+def test_expert_ffn_each_format_real_shape(fmt):
+    """moe_expert_ffn with given routing, every routed expert in one format."""
+    wl = synth.Workload(f"single_{fmt}", 20 + L.FMT[fmt], 5120, 2304, 384, 6, fmt, None, rows=(2,))
+    rows = 2
+    xbits = synth.x_bf16(wl, 0, rows, 0)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    idx = idx[:, :2].copy()                              # two experts per row keeps this quick
+    w = w[:, :2] / w[:, :2].sum(axis=1, keepdims=True)
+    w32 = w.astype(np.float32)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    dl = LY.DeviceLayer(wl, 0, materialize=need)
+    d = L.dims(wl.hidden, wl.inter, wl.n_experts, 2)
+    ws = LY.workspace(d, rows)
+    y = torch.zeros((rows, wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_expert_ffn(d, G.device_inputs(wl, 0, xbits), rows,
+                     torch.from_numpy(idx.astype(np.int32)).cuda(), torch.from_numpy(w32).cuda(),
+                     dl.weights, dl.experts, None, y, ws)
+    torch.cuda.synchronize()
+    ref = G.oracle_y(wl, 0, x, idx, w32.astype(np.float64), list(range(rows)))
+    err = G.rel_l2_rows(y.cpu().numpy(), ref)
+    _say(f"  {fmt}: rel L2 per row", err)
+    assert np.all(err <= G.REL_L2_TOL)
