@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE-layer decode tokens/s and achieved HBM GB/s on one MI355X.
+
+One step = one full pass of the layer's hot path through the C ABI
+(moe_layer: router GEMV + top-6, shared-expert gate/up, routed gate/up +
+SwiGLU, down + combine) over one batch of rows, on the real decode shape
+(hidden 5120, intermediate 2304, 384 routed Q2_0 experts, top-6, an int8
+shared expert).
+
+Inputs are synthetic and seeded, and resident in HBM before timing starts.
+Each timed step uses a different copy of the layer (8 copies, ~31 GB, so
+neither the 256 MB Infinity Cache nor the L2s can serve a step from a
+previous one) and a fresh activation row.  Routed slots are filled from a
+pool of distinct packed experts (bandwidth does not depend on the values).
+
+Prints one JSON line (see the repository's design notes for the fields).
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E, vendor figure
+METRIC = "MoE-layer decode tokens/s + achieved HBM GB/s (% of peak), rows=1..8"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--rows", type=int, default=1)
+    p.add_argument("--copies", type=int, default=8)
+    p.add_argument("--pool", type=int, default=16)
+    p.add_argument("--sweep", default="1,5,8", help="extra row counts reported beside the headline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=1)
+    return p.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b):
+        v = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return float(v.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def layer_bytes(wl, fmts_unique, rows):
+    """Algorithmic bytes of one pass: router + distinct selected experts + shared + x/y."""
+    from bit_moe_expert_02_amd import _lib as L
+    router = 4 * wl.n_experts * wl.hidden
+    per = {}
+    for f in set(fmts_unique) | ({wl.shared_fmt} if wl.shared_fmt else set()):
+        per[f] = 2 * L.packed_bytes(f, wl.inter, wl.hidden) + L.packed_bytes(f, wl.hidden, wl.inter)
+    routed = sum(per[f] for f in fmts_unique)
+    shared = per[wl.shared_fmt] if wl.shared_fmt else 0
+    return router + routed + shared + rows * wl.hidden * (2 + 4), per
+
+
+def build_copies(wl, copies, pool_n):
+    from bit_moe_expert_02_amd import layer as LY
+    from bit_moe_expert_02_amd import synth
+    pool = LY.make_pool(wl, 0, synth.format_map(wl, 0), pool_n)
+    return [LY.DeviceLayer(wl, c, materialize=(), pool=pool) for c in range(copies)]
+
+
+def run_steps(torch, L, LY, layers, xs, rows, steps, warmup, events=None, hev=None):
+    """Runs warmup + steps layer passes; returns (seconds, per-step kernel ms or None, idx list)."""
+    wl = layers[0].wl
+    ws = LY.workspace(layers[0].dims, rows)
+    idx = torch.zeros((steps + warmup, rows, wl.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((steps + warmup, rows, wl.top_k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((rows, wl.hidden), dtype=torch.float32, device="cuda")
+    evs = None
+    if events:
+        evs = hev.create(6 * steps)
+
+    def one(i, timed_slot=None):
+        dl = layers[i % len(layers)]
+        if timed_slot is None:
+            L.moe_layer(dl.dims, xs[i], rows, dl.router, dl.bias, dl.weights, dl.experts,
+                        dl.shared, idx[i], wts[i], y, ws)
+        else:
+            L.moe_layer_profiled(dl.dims, xs[i], rows, dl.router, dl.bias, dl.weights,
+                                 dl.experts, dl.shared, idx[i], wts[i], y, ws,
+                                 evs[6 * timed_slot: 6 * timed_slot + 6])
+
+    for i in range(warmup):
+        one(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        one(warmup + s, s if events else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = None
+    if events:
+        per = np.array([[hev.ms(evs[6 * s + j], evs[6 * s + j + 1]) for j in range(5)]
+                        for s in range(steps)])
+        hev.destroy(evs)
+    return t1 - t0, per, idx[warmup:].cpu().numpy()
+
+
+def cpu_baseline(wl, rows):
+    """The oracle, as it stands, on `rows` rows of layer copy 0, BLAS pinned to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    from bit_moe_expert_02_amd import synth
+    from oracle import formats as OF
+    from oracle import moe as OM
+
+    xbits = synth.x_bf16(wl, 0, rows, 999)
+    x = OM.bf16_to_f64(xbits)
+    wr = synth.router(wl, 0)
+    fm = synth.format_map(wl, 0)
+    idx, w, _, _ = OM.route(x, wr, wl.top_k, synth.bias(wl, 0))
+    packed = {}
+    for e in sorted(set(idx.reshape(-1).tolist())) + ([wl.n_experts] if wl.shared_fmt else []):
+        f = wl.shared_fmt if e == wl.n_experts else fm[e]
+        g, u, d = synth.expert_weights(wl, 0, e)
+        packed[e] = (f, OF.pack(f, g), OF.pack(f, u), OF.pack(f, d))
+
+    def expert(e):
+        f, g, u, d = packed[e]
+        return (OF.decode(f, g, wl.inter, wl.hidden), OF.decode(f, u, wl.inter, wl.hidden),
+                OF.decode(f, d, wl.hidden, wl.inter))
+
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        out = OM.moe_layer(x, wr, wl.top_k, expert,
+                           shared=expert(wl.n_experts) if wl.shared_fmt else None,
+                           bias=synth.bias(wl, 0))
+        t = time.perf_counter() - t0
+    assert np.array_equal(out["idx"], idx)
+    return dict(value=round(rows / t, 4), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{rows} row(s) of one decode_q2 layer (route + decode of the selected "
+                       f"experts and the shared expert + fp64 math), {t:.2f} s, BLAS 1 thread")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding is described in the design notes, not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from bit_moe_expert_02_amd import _lib as L
+    from bit_moe_expert_02_amd import layer as LY
+    from bit_moe_expert_02_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the MI355X"
+    L.lib()
+    wl = synth.WORKLOADS["decode_q2"]
+    hev = HipEvents()
+    print(f"[bench] building {args.copies} layer copies of {wl.name}", file=sys.stderr, flush=True)
+    layers = build_copies(wl, args.copies, args.pool)
+    torch.cuda.synchronize()
+
+    def xs_for(rows, n, base):
+        return [torch.from_numpy(synth.x_bf16(wl, 0, rows, base + i).view(np.int16).copy()).cuda()
+                for i in range(n)]
+
+    results = {}
+    sweep = sorted(set([args.rows] + [int(r) for r in args.sweep.split(",") if r]))
+    for rows in sweep:
+        n = args.steps + args.warmup
+        xs = xs_for(rows, n, 10_000 * rows)
+        secs, _, idx = run_steps(torch, L, LY, layers, xs, rows, args.steps, args.warmup)
+        uniq = [len(np.unique(i)) for i in idx]
+        fm = synth.format_map(wl, 0)
+        mean_bytes = np.mean([layer_bytes(wl, [fm[e] for e in np.unique(i)], rows)[0] for i in idx])
+        # per-kernel timing pass (events between the three kernels), same inputs
+        _, per, _ = run_steps(torch, L, LY, layers, xs, rows, args.steps, args.warmup,
+                              events=True, hev=hev)
+        results[rows] = dict(secs=secs, per=per, uniq=float(np.mean(uniq)), bytes=mean_bytes)
+        print(f"[bench] rows {rows}: {secs / args.steps * 1e6:.1f} us/step, "
+              f"kernels (route, select, gateup, down, combine) us = "
+              f"{np.round(per.mean(axis=0) * 1e3, 2).tolist()}",
+              file=sys.stderr, flush=True)
+
+    r = results[args.rows]
+    ms_step = r["secs"] / args.steps * 1e3
+    value = args.rows * args.steps / r["secs"]
+    # dominant kernel: routed gate/up (B) -- two thirds of every routed expert's bytes
+    per_fmt = layer_bytes(wl, ["Q2_0"], args.rows)[1]
+    gu_bytes = r["uniq"] * 2 * L.packed_bytes("Q2_0", wl.inter, wl.hidden)
+    b_ms = float(r["per"][:, 2].mean())
+    achieved = gu_bytes / (b_ms * 1e-3) / 1e9
+    layer_gbps = r["bytes"] / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "q2_0/q8 codes x f16 -> f32 (router f64)",
+        "data": "synthetic (seeded N(0,0.02) weights packed RTN, bf16 N(0,1) rows)",
+        "config": {
+            "workload": "decode_q2: hidden 5120, moe_intermediate 2304, 384 routed Q2_0 experts, "
+                        "top-6, 1 shared expert int8 (per-32 fp16 scale), one layer",
+            "rows": args.rows,
+            "layer_copies_rotated": args.copies,
+            "layer_bytes_per_step": int(r["bytes"]),
+            "layer_GBps": round(layer_gbps, 1),
+            "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
+            "kernel_us": {name: round(float(r["per"][:, j].mean()) * 1e3, 3) for j, name in enumerate(
+                ["route+records+shared_gateup", "select", "routed_gateup", "down", "combine"])},
+            "rows_sweep": {str(k): {"tokens_per_s": round(k * args.steps / v["secs"], 1),
+                                    "us_per_step": round(v["secs"] / args.steps * 1e6, 2),
+                                    "unique_experts": round(v["uniq"], 2),
+                                    "layer_GBps": round(v["bytes"] / (v["secs"] / args.steps) / 1e9, 1)}
+                           for k, v in results.items()},
+            "expert_bytes": {f: int(b) for f, b in per_fmt.items()},
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel": "k_gateup (routed gate/up + SwiGLU)",
+            "bytes_per_launch": int(gu_bytes),
+            "avg_launch_us": round(b_ms * 1e3, 3),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

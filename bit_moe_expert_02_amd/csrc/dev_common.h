@@ -68,11 +68,100 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Values every lane holds equally (read from LDS or computed from them),
+// moved to scalar registers so addresses built on them stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint64_t uniform(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A packed matrix as a buffer resource: a wave-uniform descriptor in scalar
+// registers, addressed with 32-bit vector offsets.  Reads at or past `bytes`
+// return zero instead of touching memory.
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+};
+__device__ __forceinline__ Buf make_buf(const uint8_t* base, uint32_t bytes) {
+  void* u = reinterpret_cast<void*>(uniform(reinterpret_cast<uint64_t>(base)));
+  return Buf{__builtin_amdgcn_make_buffer_rsrc(u, 0, static_cast<int>(bytes), 0x00020000)};
+}
+__device__ __forceinline__ u32x4 bload128(const Buf& b, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(b.r, off, 0, 0);
+  return u32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ u32x2 bload64(const Buf& b, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(b.r, off, 0, 0);
+  return u32x2{v[0], v[1]};
+}
+__device__ __forceinline__ uint32_t bload32(const Buf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(b.r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload16(const Buf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(b.r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload8(const Buf& b, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(b.r, off, 0, 0);
+}
+
 // Wave-wide (64 lanes) sum of a double via cross-lane shuffles.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
+}
+
+// Arg-max over the wave of (key, id): the larger key wins, equal keys go to
+// the lower id.  key is an order-preserving 64-bit image of a double.  DPP
+// inside each 16-lane row, then the four row winners through readlane.
+// Returns the winner in every lane.
+__device__ __forceinline__ uint64_t f64_order_key(double d) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, d);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double f64_from_order_key(uint64_t k) {
+  return __builtin_bit_cast(double, (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k);
+}
+__device__ __forceinline__ bool key_better(uint64_t ka, int ia, uint64_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(uint64_t& k, int& id) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k), CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k >> 32), CTRL, 0xF, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
+  const uint64_t ok = (static_cast<uint64_t>(hi) << 32) | lo;
+  if (key_better(ok, oi, k, id)) {
+    k = ok;
+    id = oi;
+  }
+}
+__device__ __forceinline__ void wave_argmax(uint64_t& k, int& id) {
+  argmax_step<0xB1>(k, id);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E>(k, id);   // quad_perm [2,3,0,1]
+  argmax_step<0x141>(k, id);  // row_half_mirror
+  argmax_step<0x140>(k, id);  // row_mirror: every lane holds its row's winner
+  uint64_t bk = 0;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(k), 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(k >> 32), 16 * r);
+    const int ri = __builtin_amdgcn_readlane(id, 16 * r);
+    const uint64_t rk = (static_cast<uint64_t>(hi) << 32) | lo;
+    if (r == 0 || key_better(rk, ri, bk, bi)) {
+      bk = rk;
+      bi = ri;
+    }
+  }
+  k = bk;
+  id = bi;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -54,6 +54,8 @@ __device__ __forceinline__ uint32_t make_pair(float lo, float hi, int p, float o
 // w >> 6 (i = 5,6,7 at p = 4,6,8).
 // =========================================================================
 struct FmtQ2 {
+  static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 64) * 18); }
+  static constexpr int TAG = 2;
   static constexpr int UNIT = 64, XREC = 144, PSHIFT = 6, SUBS = 4, SUBV = 16;
   static constexpr int units(int k) { return k / 64; }
   static constexpr int kP[8] = {4, 6, 8, 6, 8, 4, 6, 8};
@@ -61,12 +63,12 @@ struct FmtQ2 {
     uint32_t c[4];
     uint32_t s;
   };
-  __device__ static __forceinline__ void load(Raw& r, const uint8_t* m, int nrows, int nbu, int n,
+  __device__ static __forceinline__ void load(Raw& r, const Buf& m, int nrows, int nbu, int n,
                                               int b) {
-    const size_t bi = static_cast<size_t>(n) * nbu + b;
-    const uint4 q = *reinterpret_cast<const uint4*>(m + bi * 16);
+    const uint32_t bi = static_cast<uint32_t>(n * nbu + b);
+    const u32x4 q = bload128(m, bi * 16u);
     r.c[0] = q.x; r.c[1] = q.y; r.c[2] = q.z; r.c[3] = q.w;
-    r.s = *reinterpret_cast<const uint16_t*>(m + static_cast<size_t>(nrows) * nbu * 16 + bi * 2);
+    r.s = bload16(m, static_cast<uint32_t>(nrows * nbu * 16) + bi * 2u);
   }
   // sub-unit d = code dword d: values 16d .. 16d+15
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], int d, uint8_t* rec) {
@@ -139,20 +141,22 @@ struct FmtQ2 {
 // f16 pairs at p = 2 via (w << 2) and (w >> 6).
 // =========================================================================
 struct FmtQ8 {
+  static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 32) * 34); }
+  static constexpr int TAG = 5;
   static constexpr int UNIT = 32, XREC = 80, PSHIFT = 8, SUBS = 2, SUBV = 16;
   static constexpr int units(int k) { return k / 32; }
   struct Raw {
     uint32_t c[8];
     uint32_t s;
   };
-  __device__ static __forceinline__ void load(Raw& r, const uint8_t* m, int nrows, int nbu, int n,
+  __device__ static __forceinline__ void load(Raw& r, const Buf& m, int nrows, int nbu, int n,
                                               int b) {
-    const size_t bi = static_cast<size_t>(n) * nbu + b;
-    const uint4 q0 = *reinterpret_cast<const uint4*>(m + bi * 32);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(m + bi * 32 + 16);
+    const uint32_t bi = static_cast<uint32_t>(n * nbu + b);
+    const u32x4 q0 = bload128(m, bi * 32u);
+    const u32x4 q1 = bload128(m, bi * 32u + 16u);
     r.c[0] = q0.x; r.c[1] = q0.y; r.c[2] = q0.z; r.c[3] = q0.w;
     r.c[4] = q1.x; r.c[5] = q1.y; r.c[6] = q1.z; r.c[7] = q1.w;
-    r.s = *reinterpret_cast<const uint16_t*>(m + static_cast<size_t>(nrows) * nbu * 32 + bi * 2);
+    r.s = bload16(m, static_cast<uint32_t>(nrows * nbu * 32) + bi * 2u);
   }
   // sub-unit h = code dwords 4h .. 4h+3: values 16h .. 16h+15
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], int h, uint8_t* rec) {
@@ -224,18 +228,20 @@ struct FmtQ8 {
 // the block scale 2^(E-127) is applied to the fp32 block sum.
 // =========================================================================
 struct FmtMXFP4 {
+  static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 32) * 17); }
+  static constexpr int TAG = 4;
   static constexpr int UNIT = 32, XREC = 80, PSHIFT = 0, SUBS = 2, SUBV = 16;
   static constexpr int units(int k) { return k / 32; }
   struct Raw {
     uint32_t c[4];
     uint32_t s;
   };
-  __device__ static __forceinline__ void load(Raw& r, const uint8_t* m, int nrows, int nbu, int n,
+  __device__ static __forceinline__ void load(Raw& r, const Buf& m, int nrows, int nbu, int n,
                                               int b) {
-    const size_t bi = static_cast<size_t>(n) * nbu + b;
-    const uint4 q = *reinterpret_cast<const uint4*>(m + bi * 16);
+    const uint32_t bi = static_cast<uint32_t>(n * nbu + b);
+    const u32x4 q = bload128(m, bi * 16u);
     r.c[0] = q.x; r.c[1] = q.y; r.c[2] = q.z; r.c[3] = q.w;
-    r.s = m[static_cast<size_t>(nrows) * nbu * 16 + bi];
+    r.s = bload8(m, static_cast<uint32_t>(nrows * nbu * 16) + bi);
   }
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], int h, uint8_t* rec) {
 #pragma unroll
@@ -296,18 +302,20 @@ struct FmtMXFP4 {
 // p = 8,6,8,6 and (t4_A, t4_B) at p = 4.
 // =========================================================================
 struct FmtTern {
+  static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * ((k + 159) / 160) * 34); }
+  static constexpr int TAG = 1;
   static constexpr int UNIT = 80, XREC = 176, PSHIFT = 6, SUBS = 4, SUBV = 20;
   static constexpr int units(int k) { return 2 * ((k + 159) / 160); }
   struct Raw {
     uint32_t c[4];
     uint32_t s;
   };
-  __device__ static __forceinline__ void load(Raw& r, const uint8_t* m, int nrows, int nbu, int n,
+  __device__ static __forceinline__ void load(Raw& r, const Buf& m, int nrows, int nbu, int n,
                                               int b) {
-    const size_t bi = static_cast<size_t>(n) * nbu + b;  // unit index; block = unit / 2
-    const uint4 q = *reinterpret_cast<const uint4*>(m + bi * 16);
+    const uint32_t bi = static_cast<uint32_t>(n * nbu + b);  // unit index; block = unit / 2
+    const u32x4 q = bload128(m, bi * 16u);
     r.c[0] = q.x; r.c[1] = q.y; r.c[2] = q.z; r.c[3] = q.w;
-    r.s = *reinterpret_cast<const uint16_t*>(m + static_cast<size_t>(nrows) * nbu * 16 + (bi >> 1) * 2);
+    r.s = bload16(m, static_cast<uint32_t>(nrows * nbu * 16) + (bi >> 1) * 2u);
   }
   // table entry for byte value b (< 243); larger values decode as all-zero trits
   __device__ static __forceinline__ uint32_t table_entry(int b) {
@@ -405,6 +413,8 @@ struct FmtTern {
 // the high word shifted so that hi_i lands at p + 2.
 // =========================================================================
 struct FmtQ3 {
+  static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 256) * 110); }
+  static constexpr int TAG = 3;
   static constexpr int UNIT = 64, XREC = 144, PSHIFT = 7, SUBS = 4, SUBV = 16;
   static constexpr int units(int k) { return k / 64; }
   static constexpr int kP[8] = {3, 5, 7, 3, 5, 7, 5, 7};
@@ -414,22 +424,23 @@ struct FmtQ3 {
     uint32_t d;
     uint32_t u24;  // the unit's four 6-bit sub-scales
   };
-  __device__ static __forceinline__ void load(Raw& r, const uint8_t* m, int nrows, int nbu, int n,
+  __device__ static __forceinline__ void load(Raw& r, const Buf& m, int nrows, int nbu, int n,
                                               int b) {
-    const int ku = b & 3;
-    const size_t nb = static_cast<size_t>(nbu) >> 2;
-    const size_t blk = static_cast<size_t>(n) * nb + (b >> 2);
-    const uint8_t* cb = m + blk * 96;
-    const uint4 l = *reinterpret_cast<const uint4*>(cb + 16 * ku);
-    const uint2 h = *reinterpret_cast<const uint2*>(cb + 64 + 8 * ku);
+    const uint32_t ku = static_cast<uint32_t>(b & 3);
+    const uint32_t nb = static_cast<uint32_t>(nbu) >> 2;
+    const uint32_t blk = static_cast<uint32_t>(n) * nb + static_cast<uint32_t>(b >> 2);
+    const u32x4 l = bload128(m, blk * 96u + 16u * ku);
+    const u32x2 h = bload64(m, blk * 96u + 64u + 8u * ku);
     r.lo[0] = l.x; r.lo[1] = l.y; r.lo[2] = l.z; r.lo[3] = l.w;
     r.hi[0] = h.x; r.hi[1] = h.y;
-    const uint8_t* dplane = m + static_cast<size_t>(nrows) * nb * 96;
-    r.d = *reinterpret_cast<const uint16_t*>(dplane + blk * 2);
-    const uint32_t* ur = reinterpret_cast<const uint32_t*>(dplane + static_cast<size_t>(nrows) * nb * 2 + blk * 12);
-    const int w0 = (ku >= 2) ? 1 : 0;
-    const uint64_t pair = static_cast<uint64_t>(ur[w0]) | (static_cast<uint64_t>(ur[w0 + 1]) << 32);
-    r.u24 = static_cast<uint32_t>(pair >> (24 * ku - 32 * w0)) & 0xFFFFFFu;
+    const uint32_t dplane = static_cast<uint32_t>(nrows) * nb * 96u;
+    r.d = bload16(m, dplane + blk * 2u);
+    const uint32_t w0 = ku >= 2 ? 1u : 0u;
+    const uint32_t uo = dplane + static_cast<uint32_t>(nrows) * nb * 2u + blk * 12u + 4u * w0;
+    const uint32_t u0 = bload32(m, uo);
+    const uint32_t u1 = bload32(m, uo + 4u);
+    const uint64_t pair = static_cast<uint64_t>(u0) | (static_cast<uint64_t>(u1) << 32);
+    r.u24 = static_cast<uint32_t>(pair >> (24u * ku - 32u * w0)) & 0xFFFFFFu;
   }
   // sub-unit j = sub-block j: values 16j .. 16j+15
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], int j, uint8_t* rec) {
@@ -445,20 +456,22 @@ struct FmtQ3 {
     for (int j = 0; j < 4; ++j) {
       const int par = j & 1;
       uint32_t pr[RT][8];
+      // low 2-bit fields at p = 3, 5, 7 and the high bit at p + 2, both halves
+      constexpr uint32_t L3 = 0x00180018u, L5 = 0x00600060u, L7 = 0x01800180u;
+      constexpr uint32_t H3 = 0x00200020u, H5 = 0x00800080u, H7 = 0x02000200u;
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const uint32_t lo = raw[r].lo[j], hw = raw[r].hi[j >> 1];
         const uint32_t la = lo << 3, lb = lo >> 3, lc = lo >> 7;
         const uint32_t ha = hw << (5 - par), hb = hw >> (par + 1), hc = hw >> (par + 5);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int p = kP[i];
-          const uint32_t mlo = (3u << p) | (3u << (p + 16));
-          const uint32_t mhi = (4u << p) | (4u << (p + 16));
-          const uint32_t l = i < 3 ? la : (i < 6 ? lb : lc);
-          const uint32_t h = i < 3 ? ha : (i < 6 ? hb : hc);
-          pr[r][i] = andor(h, mhi, andor(l, mlo, kMag));
-        }
+        pr[r][0] = andor(ha, H3, andor(la, L3, kMag));
+        pr[r][1] = andor(ha, H5, andor(la, L5, kMag));
+        pr[r][2] = andor(ha, H7, andor(la, L7, kMag));
+        pr[r][3] = andor(hb, H3, andor(lb, L3, kMag));
+        pr[r][4] = andor(hb, H5, andor(lb, L5, kMag));
+        pr[r][5] = andor(hb, H7, andor(lb, L7, kMag));
+        pr[r][6] = andor(hc, H5, andor(lc, L5, kMag));
+        pr[r][7] = andor(hc, H7, andor(lc, L7, kMag));
       }
       float bd[RT][NT];
 #pragma unroll

@@ -144,7 +144,7 @@ typedef struct {
 } moe_expert_ref;
 
 /* Supported shapes: (hidden, inter) = (5120, 2304) or (512, 256);
- * 1 <= top_k <= MOE_MAX_TOP_K, top_k <= n_experts <= 4096,
+ * 1 <= top_k <= MOE_MAX_TOP_K, top_k <= n_experts <= 512,
  * rows * top_k <= 64, rows <= MOE_MAX_DECODE_ROWS.  Returns 0 for
  * unsupported dims. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows);
@@ -164,10 +164,9 @@ int moe_check_experts(const moe_dims* dims, const moe_expert_ref* table, int32_t
  *   idx      [rows x top_k] int32, device, out: selected ids, key desc / id asc
  *   wts      [rows x top_k] fp32, device, out: mixing weights (unbiased softmax
  *            renormalised over the selection)
- *   ws       device workspace of ws_bytes >= moe_workspace_bytes(dims, rows).
- *            It must be zero-filled before its first use; every call leaves it
- *            ready for the next.  One workspace must not serve two calls that
- *            can overlap.
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(dims, rows);
+ *            its contents need no initialisation.  One workspace must not
+ *            serve two calls that can overlap.
  * rows == 0 returns MOE_OK and launches nothing. */
 int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, int32_t* idx, float* wts, void* ws, size_t ws_bytes,
@@ -195,10 +194,11 @@ int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const floa
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
               size_t ws_bytes, void* stream);
 
-/* moe_layer with timing: `events` holds n_events >= 4 hipEvent_t handles
+/* moe_layer with timing: `events` holds n_events >= 6 hipEvent_t handles
  * created by the caller.  events[0] is recorded before the first kernel and
- * events[i] after the i-th of the layer's three kernels (router + shared
- * gate/up, routed gate/up, down + combine). */
+ * events[i] after the i-th of the layer's five kernels: (1) router GEMV,
+ * activation records and shared-expert gate/up, (2) top-k selection,
+ * (3) routed gate/up + SwiGLU, (4) down projections, (5) combine. */
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        const float* w_router, const float* sel_bias, const void* weights,
                        const moe_expert_ref* experts, const moe_expert_ref* shared,

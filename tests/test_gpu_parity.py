@@ -63,6 +63,7 @@ def test_tiny_deterministic_and_workspace_reuse():
     dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
     ys = []
     ws = LY.workspace(dl.dims, 8)
+    ws.fill_(0xA5)                                 # contents need no initialisation
     for rep, stream in enumerate([10, 11, 10]):
         xbits = synth.x_bf16(wl, 0, 8, stream)
         xd = G.device_inputs(wl, 0, xbits)
@@ -77,8 +78,6 @@ def test_tiny_deterministic_and_workspace_reuse():
         assert np.array_equal(idx.cpu().numpy(), ri)
         assert np.all(G.rel_l2_rows(ys[-1], G.oracle_y(wl, 0, x, ri, rw, list(range(8)))) <= G.REL_L2_TOL)
     assert np.array_equal(ys[0], ys[2])            # bitwise reproducible
-    # the workspace's counters are back at zero after every call
-    assert not torch.any(ws[: 4 * 1025].view(torch.int32)).item()
 
 
 def test_route_only_and_ffn_only_match_layer():
