@@ -7,7 +7,7 @@ decoders and layer arithmetic are written here, in NumPy, from the format
 definitions and the method as the source pages describe it.
 
 Sources (cited by page title and section):
-  [P1] "Three architectures for one DeepSeek-V4.1-Flash on 4xL20"
+  [P1] "DeepSeek-V4.1-Flash served three ways on 4xL20"
        (lcz.me/topic/2356): §1 model structure, §2 bytes-per-token arithmetic,
        §3B Strata verify law, §7 measurement discipline.
   [P3] "[Strata] DeepSeek V4.1 Flash on a single 4090" (lcz.me/post/25274):
