@@ -49,8 +49,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) {
 }
 
 // Sum of v over groups of LPR consecutive lanes (LPR in {1,2,4,8,16}); every
-// lane of a group ends with the group's sum.  DPP moves stay inside a row of
-// 16 lanes: quad swaps, then half-row and full-row mirrors.
+// lane of a group ends with the group's sum.  Up to 16 lanes, DPP moves inside
+// a row: quad swaps, then half-row and full-row mirrors.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LPR >= 2)
@@ -65,6 +65,9 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (LPR >= 16)
     v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                               0x140, 0xF, 0xF, false));
+  // wider groups leave the 16-lane row: lane permutes through LDS hardware
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
   return v;
 }
 
@@ -175,15 +178,66 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 // Loads that read what other workgroups published in this kernel (through
 // device-scope release/acquire); they bypass non-coherent caches.
-__device__ __forceinline__ float coherent_load_f32(const float* p) {
-  return __builtin_bit_cast(
-      float, __hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT));
+// ---------------------------------------------------------------------------
+// Tagged words: hand-offs between workgroups of one launch without fences.
+// A word is (tag << 32) | payload, written and read with relaxed atomics at
+// agent scope, which keep every single word coherent across the XCDs' L2s.
+// A consumer takes a word once its tag equals the call's tag, so no ordering
+// between different words is needed and no cache write-back is issued.  The
+// tag is per call (an epoch kept in the workspace), so words left by earlier
+// calls never look ready.
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 16;   // polls before a wait gives up (tens of ms)
+
+__device__ __forceinline__ uint64_t tload(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ double coherent_load_f64(const double* p) {
-  return __builtin_bit_cast(
-      double, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ void tstore(uint64_t* p, uint32_t tag, uint32_t v) {
+  __hip_atomic_store(p, (static_cast<uint64_t>(tag) << 32) | v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// N words at once: addr(j) gives word j's address, or null for none (then its
+// payload reads 0).  All loads are issued together; only the words not yet
+// carrying `tag` are polled again.  Payloads land in out[].
+template <int N, class AddrF>
+__device__ __forceinline__ void await_batch(AddrF addr, uint32_t tag, uint32_t* err,
+                                            uint32_t (&out)[N]) {
+  uint64_t w[N];
+  const uint64_t ready0 = static_cast<uint64_t>(tag) << 32;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const uint64_t* p = addr(j);
+    w[j] = p ? tload(p) : ready0;
+  }
+  for (int it = 0;; ++it) {
+    bool all = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) all = all && static_cast<uint32_t>(w[j] >> 32) == tag;
+    if (all) break;
+    if (it >= kSpinLimit) {
+      __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (static_cast<uint32_t>(w[j] >> 32) != tag) w[j] = tload(addr(j));
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) out[j] = static_cast<uint32_t>(w[j]);
+}
+
+// Payload of *p once it carries `tag`.  After kSpinLimit polls the wait ends,
+// *err is set to `tag` and 0 is returned: a launch always drains, and the
+// failure is recorded for that call in the error word.
+__device__ __forceinline__ uint32_t await_word(const uint64_t* p, uint32_t tag, uint32_t* err) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    const uint64_t w = tload(p);
+    if (static_cast<uint32_t>(w >> 32) == tag) return static_cast<uint32_t>(w);
+    __builtin_amdgcn_s_sleep(8);
+  }
+  __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0u;
 }
 
 }  // namespace dev

@@ -49,6 +49,9 @@ constexpr int kMaxSlots = 64;                  // distinct routed experts per ca
 constexpr int kNumFmt = 5;                     // format tags 1..5
 constexpr int kPrepWGs = 16;                   // workgroups building activation records
 constexpr int kSelQ = 8;                       // experts per lane in the selection (E <= 512)
+// A published selection entry of the fused launch, as tagged words: id | fmt << 16,
+// weight bits, then the gate, up and down offsets of the expert (low, high).
+constexpr int kSelWords = 8;
 
 // One entry of the slot table: a distinct selected expert (or the shared one)
 // and the rows it serves.
@@ -61,10 +64,17 @@ struct SlotEntry {
   float w[kMaxRows];        // mixing weight (1 for the shared expert)
 };
 
+// The work of one call: slots [0, n_active) are the distinct routed experts in
+// ascending id, slot n_active the shared expert (when there is one).  Work
+// item i of the gate/up (down) launch is tile i - gu_off[s] of the slot s with
+// gu_off[s] <= i < gu_off[s + 1]; tile counts depend on each slot's format.
 struct SlotTable {
   int n_active;             // distinct routed experts in this call
-  int pad[3];
-  SlotEntry e[kMaxSlots];
+  int n_slots;              // n_active, plus one for the shared expert
+  int n_gu, n_dn;           // work items of the gate/up and down launches
+  int gu_off[kMaxSlots + 2];
+  int dn_off[kMaxSlots + 2];
+  SlotEntry e[kMaxSlots + 1];
 };
 
 struct Args {
@@ -86,45 +96,105 @@ struct Args {
   float* part;                    // [(R*k + R) x H]
   int xrow;                       // bytes of one (format, row) record block
   int R, k, E;
-  int shared_early;               // 1: the shared expert's gate/up rides with the selection
-                                  // and its down with the routed gate/up (moe_layer)
+  // fused layer (one launch for route, select, gate/up and down): tagged
+  // hand-off words and the layout of the workgroup roles
+  uint32_t* epoch;                // [2] epoch[0]: a fused call runs with tag epoch[0] + 1 and
+                                  // records it in epoch[1]; its combine copies it to epoch[0]
+  uint32_t* err;                  // [1] the tag of a call in which a wait gave up
+  uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
+  uint64_t* selt;                 // [R x k x kSelWords] selection entries (see kSelWords)
+  uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
+  int base_b, nb, base_c, nc;     // gate/up and down worker ranges of the fused launch
+  int shared_early;               // 1: the shared expert's gate/up runs beside the router
+                                  // (moe_layer), so the gate/up launch skips it
 };
 
 // ---------------------------------------------------------------------------
-// shape-dependent constants
+// tile shapes
 // ---------------------------------------------------------------------------
-constexpr int lpr_for(int k) { return k >= 4096 ? 16 : (k >= 512 ? 8 : 4); }
+// How one workgroup covers a matrix of format F with reduction length K: LPR
+// lanes share a group of NPG channels (rows of the matrix); a workgroup owns
+// TN consecutive channels.  LPR is the smallest power of two that lets every
+// lane issue all of its loads at once within kLaneBudget bytes of registers,
+// so a tile costs one round trip to HBM however heavy its format is; a
+// format with few bytes per channel gives each lane group two channels
+// instead of fewer than 8 lanes, which keeps 128-byte runs per load.
+constexpr int kLaneBudget = 216;
 
-template <class F>
-constexpr int phase_units() {
-  return sizeof(typename F::Raw) > 28 ? 2 : 5;  // units per load phase: bounds the registers
-}
+template <class F, int K, bool GU>
+struct TileCfg {
+  static constexpr int NBU = F::units(K);
+  static constexpr int RAW = static_cast<int>(sizeof(typename F::Raw));
+  static constexpr int RTC = GU ? 2 : 1;  // matrices per channel (gate and up)
+  static constexpr int lpr0() {
+    int l = 1;
+    while (l < 64 && ((NBU + l - 1) / l) * RTC * RAW > kLaneBudget) l *= 2;
+    return l;
+  }
+  static constexpr int pow2_floor(int v) {
+    int p = 1;
+    while (p * 2 <= v) p *= 2;
+    return p;
+  }
+  static constexpr int LPR_MIN = NBU >= 8 ? 8 : pow2_floor(NBU);
+  static constexpr int LPR = lpr0() > LPR_MIN ? lpr0() : LPR_MIN;
+  static constexpr int NPG = (!GU && lpr0() * 2 <= LPR) ? 2 : 1;
+  static constexpr int RT = RTC * NPG;     // matrix rows per lane
+  static constexpr int TN = kThreads / LPR * NPG;
+  static constexpr int UPL = (NBU + LPR - 1) / LPR;
+  static constexpr int g0() {
+    int g = UPL;
+    while (g > 1 && g * RT * RAW > kLaneBudget) --g;
+    return g;
+  }
+  static constexpr int G = g0();           // units per load phase
+  static_assert(kThreads % LPR == 0 && LPR <= 64, "lane groups must tile a wave");
+};
 
 template <int H, int I>
 struct Shape {
   static constexpr int kH = H, kI = I;
-  static constexpr int LPR_GU = lpr_for(H), LPR_DN = lpr_for(I);
-  static constexpr int NPG_GU = 1, NPG_DN = 2;  // channels per lane group
-  static constexpr int TN_GU = kThreads / LPR_GU * NPG_GU;
-  static constexpr int TN_DN = kThreads / LPR_DN * NPG_DN;
-  static constexpr int TILES_GU = (I + TN_GU - 1) / TN_GU;
-  static constexpr int TILES_DN = (H + TN_DN - 1) / TN_DN;
+  template <class F>
+  static constexpr int tiles_gu() { return (I + TileCfg<F, H, true>::TN - 1) / TileCfg<F, H, true>::TN; }
+  template <class F>
+  static constexpr int tiles_dn() { return (H + TileCfg<F, I, false>::TN - 1) / TileCfg<F, I, false>::TN; }
+  static constexpr int cmax(int a, int b) { return a > b ? a : b; }
+  static constexpr int MAX_TILES_GU =
+      cmax(cmax(cmax(tiles_gu<FmtQ2>(), tiles_gu<FmtQ8>()), cmax(tiles_gu<FmtMXFP4>(), tiles_gu<FmtTern>())),
+           tiles_gu<FmtQ3>());
+  static constexpr int MAX_TILES_DN =
+      cmax(cmax(cmax(tiles_dn<FmtQ2>(), tiles_dn<FmtQ8>()), cmax(tiles_dn<FmtMXFP4>(), tiles_dn<FmtTern>())),
+           tiles_dn<FmtQ3>());
   template <class F>
   static constexpr int rec_row_bytes(int k) { return F::units(k) * F::XREC; }
   static constexpr int max_rec_row(int k) {
-    int m = rec_row_bytes<FmtQ2>(k);
-    m = m > rec_row_bytes<FmtQ8>(k) ? m : rec_row_bytes<FmtQ8>(k);
-    m = m > rec_row_bytes<FmtMXFP4>(k) ? m : rec_row_bytes<FmtMXFP4>(k);
-    m = m > rec_row_bytes<FmtTern>(k) ? m : rec_row_bytes<FmtTern>(k);
-    m = m > rec_row_bytes<FmtQ3>(k) ? m : rec_row_bytes<FmtQ3>(k);
-    return m;
+    return cmax(cmax(cmax(rec_row_bytes<FmtQ2>(k), rec_row_bytes<FmtQ8>(k)),
+                     cmax(rec_row_bytes<FmtMXFP4>(k), rec_row_bytes<FmtTern>(k))),
+                rec_row_bytes<FmtQ3>(k));
   }
   static constexpr int XROW = max_rec_row(H);   // one (format, row) block of x records
   // LDS: token-row records, then the ternary decode table
-  static constexpr int LDS_REC = kNTB * (max_rec_row(H) > max_rec_row(I) ? max_rec_row(H) : max_rec_row(I));
+  static constexpr int LDS_REC = kNTB * cmax(max_rec_row(H), max_rec_row(I));
   static constexpr int LDS_TABLE = 256 * 4;
   static constexpr int LDS_BYTES = LDS_REC + LDS_TABLE;
+  // staging of raw activations: x rows (bf16) for locally built gate/up
+  // records, or h rows (fp32) handed over inside the fused launch
+  static constexpr int LDS_STAGE = cmax(kNTB * I * 4, kNTB * H * 2);
+  static constexpr int LDS_WITH_STAGE = LDS_BYTES + LDS_STAGE;
 };
+
+// tiles of a format tag (device side: the tag comes from the expert table)
+template <class S, bool GU>
+__device__ __forceinline__ int tiles_of(uint32_t fmt) {
+  switch (fmt) {
+    case MOE_FMT_Q2_0: return GU ? S::template tiles_gu<FmtQ2>() : S::template tiles_dn<FmtQ2>();
+    case MOE_FMT_Q8: return GU ? S::template tiles_gu<FmtQ8>() : S::template tiles_dn<FmtQ8>();
+    case MOE_FMT_MXFP4: return GU ? S::template tiles_gu<FmtMXFP4>() : S::template tiles_dn<FmtMXFP4>();
+    case MOE_FMT_TERN160: return GU ? S::template tiles_gu<FmtTern>() : S::template tiles_dn<FmtTern>();
+    case MOE_FMT_Q3: return GU ? S::template tiles_gu<FmtQ3>() : S::template tiles_dn<FmtQ3>();
+    default: return 0;
+  }
+}
 
 // ---------------------------------------------------------------------------
 // activation records
@@ -167,7 +237,7 @@ __device__ __forceinline__ int sigma_exp(uint32_t max_bits) {
 // Largest |value| of a row, as monotone fp32 bits; called by every thread of
 // the workgroup, result valid in all threads.
 template <int KR, bool BF16>
-__device__ uint32_t row_max_bits(const void* src, uint32_t* red) {
+__device__ __forceinline__ uint32_t row_max_bits(const void* src, uint32_t* red) {
   constexpr int PER = BF16 ? 8 : 4;
   constexpr int CH = (KR / PER + kThreads - 1) / kThreads;
   uint4 qs[CH];
@@ -240,11 +310,10 @@ __device__ __forceinline__ void dot_unit(const typename F::Raw (&raw)[RT], const
 // Streams the lane's units of RT matrix rows (mats[r], row rows[r]) and
 // accumulates them against the staged records.  Phase 0 is loaded by
 // load_first() so the caller can overlap it with record staging.
-template <class F, int K, int LPR, int RT>
+template <class F, int K, int LPR, int RT, int G>
 struct Stream {
   static constexpr int NBU = F::units(K);
   static constexpr int UPL = (NBU + LPR - 1) / LPR;
-  static constexpr int G = phase_units<F>() < UPL ? phase_units<F>() : UPL;
   static constexpr int P = (UPL + G - 1) / G;
   typename F::Raw raw[2][G][RT];
 
@@ -292,9 +361,10 @@ __device__ __forceinline__ void build_tern_table(uint32_t* table) {
 // STAGE_LOCAL: records are built here from x (shared expert riding in the
 // router launch); otherwise they are copied from the per-layer record buffer.
 // ---------------------------------------------------------------------------
-template <class S, class F, bool STAGE_LOCAL>
-__device__ void gateup_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds) {
-  constexpr int H = S::kH, I = S::kI, LPR = S::LPR_GU;
+template <class S, class F, bool STAGE_LOCAL, bool TAG>
+__device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds, uint32_t tag) {
+  using C = TileCfg<F, S::kH, true>;
+  constexpr int H = S::kH, I = S::kI, LPR = C::LPR;
   constexpr int RSTRIDE = F::units(H) * F::XREC;
   uint8_t* rec = lds;
   uint32_t* table = reinterpret_cast<uint32_t*>(lds + S::LDS_REC);
@@ -304,27 +374,64 @@ __device__ void gateup_tile(const Args& a, const SlotEntry& sl, int tile, uint8_
   __shared__ const void* srcs[kNTB];
   build_tern_table<F>(table);
   const int rg = threadIdx.x / LPR, c = threadIdx.x % LPR;
-  const int n = tile * S::TN_GU + rg;
+  const int n = tile * C::TN + rg;
   const bool valid = n < I;
   const Buf mats[2] = {make_buf(a.weights + sl.ref.gate, F::bytes(I, H)),
                        make_buf(a.weights + sl.ref.up, F::bytes(I, H))};
   const int rows[2] = {n, n};
-  Stream<F, H, LPR, 2> st;
+  Stream<F, H, LPR, 2, C::G> st;
   const int fi = uniform(static_cast<int>(sl.ref.fmt) - 1);
   const int nt_all = uniform(sl.nt);
   for (int t0 = 0; t0 < nt_all; t0 += kNTB) {
     const int nb = nt_all - t0 < kNTB ? nt_all - t0 : kNTB;
+    // local records: the x rows are loaded before the weights, so the
+    // records are built while the weights are still in flight and one round
+    // trip to memory covers both
+    constexpr int XCH = (H / 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread and row
+    uint4 xq[kNTB][XCH];
+    if constexpr (STAGE_LOCAL) {
+#pragma unroll
+      for (int t = 0; t < kNTB; ++t)
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+          const int ch = threadIdx.x + i * kThreads;
+          xq[t][i] = (t < nb && ch < H / 8)
+                         ? *reinterpret_cast<const uint4*>(a.x + static_cast<size_t>(sl.row[t0 + t]) * H + 8 * ch)
+                         : uint4{0u, 0u, 0u, 0u};
+        }
+    }
     st.load(0, mats, rows, I, valid);            // weights in flight while records are staged
     __syncthreads();
     if constexpr (STAGE_LOCAL) {
-      if (threadIdx.x < nb) srcs[threadIdx.x] = a.x + static_cast<size_t>(sl.row[t0 + threadIdx.x]) * H;
-      __syncthreads();
-      for (int t = 0; t < nb; ++t) {
-        const uint32_t m = row_max_bits<H, true>(srcs[t], red);
-        if (threadIdx.x == 0) {
-          sig_exp[t] = sigma_exp<F>(m);
-          inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
+      uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
+#pragma unroll
+      for (int t = 0; t < kNTB; ++t) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+          const int ch = threadIdx.x + i * kThreads;
+          if (t < nb && ch < H / 8) {
+            *reinterpret_cast<uint4*>(xs + t * H + 8 * ch) = xq[t][i];
+            const uint32_t w[4] = {xq[t][i].x, xq[t][i].y, xq[t][i].z, xq[t][i].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t lo = (w[q] & 0x7FFFu) << 16, hi = (w[q] >> 16 & 0x7FFFu) << 16;
+              m = m > lo ? m : lo;
+              m = m > hi ? m : hi;
+            }
+          }
         }
+        m = wave_max_u32(m);
+        if ((threadIdx.x & 63) == 0) red[t * 4 + (threadIdx.x >> 6)] = m;
+      }
+      __syncthreads();
+      if (threadIdx.x < nb) {
+        const int t = threadIdx.x;
+        uint32_t m = 0;
+        for (int w = 0; w < kThreads / 64; ++w) m = m > red[t * 4 + w] ? m : red[t * 4 + w];
+        sig_exp[t] = sigma_exp<F>(m);
+        inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
+        srcs[t] = xs + t * H;
       }
       __syncthreads();
       build_records<F, H, true>(srcs, nb, sig_exp, rec, threadIdx.x, blockDim.x);
@@ -360,16 +467,21 @@ __device__ void gateup_tile(const Args& a, const SlotEntry& sl, int tile, uint8_
       if (t < nb) {
         const float g = acc[0][t] * inv_sigma[t], v = acc[1][t] * inv_sigma[t];
         const float hv = g / (1.0f + expf(-g)) * v;
-        if (valid && c == 0) a.h[static_cast<size_t>(sl.pair[t0 + t]) * I + n] = hv;
+        if (valid && c == 0) {
+          const size_t o = static_cast<size_t>(sl.pair[t0 + t]) * I + n;
+          if constexpr (TAG) tstore(a.ht + o, tag, __builtin_bit_cast(uint32_t, hv));
+          else a.h[o] = hv;
+        }
       }
     }
   }
 }
 
 // down tile: outputs [tile*TN, tile*TN + TN) of H for every row of the slot
-template <class S, class F>
-__device__ void down_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds) {
-  constexpr int H = S::kH, I = S::kI, LPR = S::LPR_DN, NPG = S::NPG_DN;
+template <class S, class F, bool TAG>
+__device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds, uint32_t tag) {
+  using C = TileCfg<F, S::kI, false>;
+  constexpr int H = S::kH, I = S::kI, LPR = C::LPR, NPG = C::NPG;
   uint8_t* rec = lds;
   uint32_t* table = reinterpret_cast<uint32_t*>(lds + S::LDS_REC);
   __shared__ float inv_sigma[kNTB];
@@ -378,18 +490,49 @@ __device__ void down_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t*
   __shared__ const void* srcs[kNTB];
   build_tern_table<F>(table);
   const int rg = threadIdx.x / LPR, c = threadIdx.x % LPR;
-  const int n0 = tile * S::TN_DN + rg * NPG;
+  const int n0 = tile * C::TN + rg * NPG;
   const Buf md = make_buf(a.weights + sl.ref.down, F::bytes(H, I));
-  const Buf mats[NPG] = {md, md};
-  const int rows[NPG] = {n0, n0 + 1};
-  const bool valid = n0 + NPG <= H;
-  Stream<F, I, LPR, NPG> st;
+  Buf mats[NPG];
+  int rows[NPG];
+#pragma unroll
+  for (int q = 0; q < NPG; ++q) {
+    mats[q] = md;
+    rows[q] = n0 + q;
+  }
+  const bool valid = n0 + NPG <= H;   // H is a multiple of NPG
+  Stream<F, I, LPR, NPG, C::G> st;
   const int nt_all = uniform(sl.nt);
   for (int t0 = 0; t0 < nt_all; t0 += kNTB) {
     const int nb = nt_all - t0 < kNTB ? nt_all - t0 : kNTB;
     st.load(0, mats, rows, H, valid);
     __syncthreads();
-    if (threadIdx.x < nb) srcs[threadIdx.x] = a.h + static_cast<size_t>(sl.pair[t0 + threadIdx.x]) * I;
+    if constexpr (TAG) {
+      // h comes from gate/up workgroups of the same launch: wait for its
+      // tagged words and stage the values in LDS
+      float* hs = reinterpret_cast<float*>(lds + S::LDS_BYTES);
+      constexpr int PER = (I + kThreads - 1) / kThreads;
+      for (int t = 0; t < nb; ++t) {
+        const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
+        // first a sparse wait (one word in every I/kThreads, which samples
+        // every gate/up tile of 16 channels), then the whole vector once
+        (void)await_word(src + (threadIdx.x * (I / kThreads)), tag, a.err);
+        uint32_t v[PER];
+        await_batch<PER>(
+            [src](int j) -> const uint64_t* {
+              const int i = threadIdx.x + j * kThreads;
+              return i < I ? src + i : nullptr;
+            },
+            tag, a.err, v);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int i = threadIdx.x + j * kThreads;
+          if (i < I) hs[t * I + i] = __builtin_bit_cast(float, v[j]);
+        }
+      }
+      if (threadIdx.x < nb) srcs[threadIdx.x] = hs + threadIdx.x * I;
+    } else {
+      if (threadIdx.x < nb) srcs[threadIdx.x] = a.h + static_cast<size_t>(sl.pair[t0 + threadIdx.x]) * I;
+    }
     __syncthreads();
     for (int t = 0; t < nb; ++t) {
       const uint32_t m = row_max_bits<I, false>(srcs[t], red);
@@ -421,12 +564,14 @@ __device__ void down_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t*
   }
 }
 
-template <class S, int STAGE>  // STAGE: 0 down, 1 gate/up from records, 2 gate/up staged locally
-__device__ void run_slot(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds) {
-#define MOE_RUN_FMT(TAG, FT)                                                    \
-  case TAG:                                                                    \
-    if constexpr (STAGE == 0) down_tile<S, FT>(a, sl, tile, lds);              \
-    else gateup_tile<S, FT, STAGE == 2>(a, sl, tile, lds);                     \
+// STAGE: 0 down, 1 gate/up from records, 2 gate/up staged locally.
+// TAG: h is handed over as tagged words (fused launch).
+template <class S, int STAGE, bool TAG = false>
+__device__ __forceinline__ void run_slot(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds, uint32_t tag = 0) {
+#define MOE_RUN_FMT(FTAG, FT)                                                  \
+  case FTAG:                                                                   \
+    if constexpr (STAGE == 0) down_tile<S, FT, TAG>(a, sl, tile, lds, tag);    \
+    else gateup_tile<S, FT, STAGE == 2, TAG>(a, sl, tile, lds, tag);           \
     break;
   switch (sl.ref.fmt) {
     MOE_RUN_FMT(MOE_FMT_Q2_0, FmtQ2)
@@ -444,9 +589,13 @@ __device__ void run_slot(const Args& a, const SlotEntry& sl, int tile, uint8_t* 
 // per-layer preparation: slot table and activation records
 // ---------------------------------------------------------------------------
 // Distinct experts of the routing in ascending id, each with the rows that
-// chose it, and every row's k entries in ascending id.  Run by wave 0; ids
-// and weights come from LDS (ids[R*k], wv[R*k]).
-__device__ void build_slot_table(const Args& a, const int* ids, const float* wv) {
+// chose it, every row's k entries in ascending id, then the shared expert's
+// slot and the work-item offsets of both launches.  Run by wave 0; ids and
+// weights come from LDS (ids[R*k], wv[R*k]).
+template <class S>
+__device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, const float* wv, SlotTable* tab,
+                                 bool write_order, const moe_expert_ref* eref = nullptr) {
+  __shared__ int tg[kMaxSlots + 1], td[kMaxSlots + 1];
   const int lane = threadIdx.x;
   const int n = a.R * a.k;
   const int v = lane < n ? ids[lane] : 0x7fffffff;
@@ -459,9 +608,11 @@ __device__ void build_slot_table(const Args& a, const int* ids, const float* wv)
   const uint64_t firsts = __ballot(first);
   for (int m = 0; m < n; ++m)
     if (((firsts >> m) & 1ull) && ids[m] < v) ++rank;
+  const int n_active = __popcll(firsts);
   if (first) {
-    SlotEntry& e = a.slots->e[rank];
-    e.ref = a.experts[v];
+    SlotEntry& e = tab->e[rank];
+    const moe_expert_ref ref = eref ? eref[lane] : a.experts[v];
+    e.ref = ref;
     e.expert = v;
     int t = 0;
     for (int m = 0; m < n && t < kMaxRows; ++m) {  // distinct ids per row bound t by R
@@ -473,8 +624,24 @@ __device__ void build_slot_table(const Args& a, const int* ids, const float* wv)
       }
     }
     e.nt = t;
+    tg[rank] = tiles_of<S, true>(ref.fmt);
+    td[rank] = tiles_of<S, false>(ref.fmt);
   }
-  if (lane < a.R) {
+  if (a.shared && lane < a.R) {
+    SlotEntry& e = tab->e[n_active];
+    if (lane == 0) {
+      const moe_expert_ref ref = *a.shared;
+      e.ref = ref;
+      e.expert = -1;
+      e.nt = a.R;
+      tg[n_active] = a.shared_early ? 0 : tiles_of<S, true>(ref.fmt);
+      td[n_active] = tiles_of<S, false>(ref.fmt);
+    }
+    e.row[lane] = lane;
+    e.pair[lane] = n + lane;
+    e.w[lane] = 1.0f;
+  }
+  if (write_order && lane < a.R) {
     const int* row = ids + lane * a.k;
     for (int j = 0; j < a.k; ++j) {   // position of entry j = number of smaller ids in the row
       int pos = 0;
@@ -482,13 +649,30 @@ __device__ void build_slot_table(const Args& a, const int* ids, const float* wv)
       a.order[lane * a.k + pos] = j;
     }
   }
-  if (lane == 0) a.slots->n_active = __popcll(firsts);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");  // LDS tile counts visible to lane 0
+  if (lane == 0) {
+    const int ns = n_active + (a.shared ? 1 : 0);
+    int og = 0, od = 0;
+    for (int q = 0; q < ns; ++q) {
+      tab->gu_off[q] = og;
+      tab->dn_off[q] = od;
+      og += tg[q];
+      od += td[q];
+    }
+    tab->gu_off[ns] = og;
+    tab->dn_off[ns] = od;
+    tab->n_active = n_active;
+    tab->n_slots = ns;
+    tab->n_gu = og;
+    tab->n_dn = od;
+  }
 }
 
 // Activation records of every format for every row, built by kPrepWGs
 // workgroups (p = 0 .. kPrepWGs-1).
 template <class S, class F>
-__device__ void prep_format(const Args& a, int p, const int* sig_base) {
+__device__ __forceinline__ void prep_format(const Args& a, int p, const int* sig_base) {
   constexpr int H = S::kH;
   const int fi = F::TAG - 1;
   __shared__ int sig_exp[kMaxRows];
@@ -507,7 +691,7 @@ __device__ void prep_format(const Args& a, int p, const int* sig_base) {
 }
 
 template <class S>
-__device__ void prep_wg(const Args& a, int p) {
+__device__ __forceinline__ void prep_wg(const Args& a, int p) {
   __shared__ uint32_t red[16];
   __shared__ int base[kMaxRows];
   for (int r = 0; r < a.R; ++r) {
@@ -526,7 +710,7 @@ __device__ void prep_wg(const Args& a, int p) {
 // router GEMV + top-k
 // ---------------------------------------------------------------------------
 template <int H>
-__device__ void router_wg(const Args& a, int e, double* red) {
+__device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uint32_t tag = 0) {
   constexpr int CH = (H / 4 + kThreads - 1) / kThreads;   // float4 chunks per thread
   double acc[kMaxRows];
 #pragma unroll
@@ -571,24 +755,59 @@ __device__ void router_wg(const Args& a, int e, double* red) {
   if (threadIdx.x < a.R) {
     double s = 0.0;
     for (int w = 0; w < nw; ++w) s += red[threadIdx.x * 16 + w];
-    a.logits[static_cast<size_t>(threadIdx.x) * a.E + e] = s;
+    const size_t o = static_cast<size_t>(threadIdx.x) * a.E + e;
+    if (a.lgt) {   // fused launch: publish as two tagged halves
+      const uint64_t b = __builtin_bit_cast(uint64_t, s);
+      tstore(a.lgt + 2 * o, tag, static_cast<uint32_t>(b));
+      tstore(a.lgt + 2 * o + 1, tag, static_cast<uint32_t>(b >> 32));
+    } else {
+      a.logits[o] = s;
+    }
   }
 }
 
 // Top-k of one row by key = logit + bias, ties to the lower id; weights are
 // the softmax of the unbiased logits over the selection.  One wave per row;
 // the logits come from the previous kernel, so plain loads see them.
-__device__ void select_row(const Args& a, int r, int* sel, float* wsel) {
+__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ], int* sel, float* wsel,
+                            uint32_t tag, const moe_expert_ref* refs);
+
+__device__ __forceinline__ void select_row(const Args& a, int r, int* sel, float* wsel) {
   const int lane = threadIdx.x & 63;
   const double* lg = a.logits + static_cast<size_t>(r) * a.E;
-  // every logit and key of the lane in registers before the k rounds
   double lv[kSelQ];
-  uint64_t kv[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const int e = lane + 64 * q;
     lv[q] = e < a.E ? lg[e] : 0.0;
   }
+  select_core(a, r, lv, sel, wsel, 0, nullptr);
+}
+
+// The fused launch: the row's logits arrive as tagged halves from the router
+// workgroups of the same launch.
+__device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel, float* wsel, uint32_t tag,
+                                  const moe_expert_ref* refs) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t* lg = a.lgt + static_cast<size_t>(r) * a.E * 2;
+  uint32_t half[2 * kSelQ];
+  await_batch<2 * kSelQ>(
+      [lg, lane, E = a.E](int j) -> const uint64_t* {
+        const int e = lane + 64 * (j >> 1);
+        return e < E ? lg + 2 * e + (j & 1) : nullptr;
+      },
+      tag, a.err, half);
+  double lv[kSelQ];
+#pragma unroll
+  for (int q = 0; q < kSelQ; ++q)
+    lv[q] = __builtin_bit_cast(double, (static_cast<uint64_t>(half[2 * q + 1]) << 32) | half[2 * q]);
+  select_core(a, r, lv, sel, wsel, tag, refs);
+}
+
+__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ], int* sel, float* wsel,
+                            uint32_t tag, const moe_expert_ref* refs) {
+  const int lane = threadIdx.x & 63;
+  uint64_t kv[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const int e = lane + 64 * q;
@@ -639,6 +858,18 @@ __device__ void select_row(const Args& a, int r, int* sel, float* wsel) {
     wsel[lane] = w;
     a.idx[r * a.k + lane] = my_id;
     a.wts[r * a.k + lane] = w;
+    if (a.selt) {   // fused launch: publish the entry with its expert's matrices
+      uint64_t* o = a.selt + kSelWords * static_cast<size_t>(r * a.k + lane);
+      const moe_expert_ref& f = refs[my_id];
+      tstore(o, tag, static_cast<uint32_t>(my_id) | (f.fmt << 16));
+      tstore(o + 1, tag, __builtin_bit_cast(uint32_t, w));
+      tstore(o + 2, tag, static_cast<uint32_t>(f.gate));
+      tstore(o + 3, tag, static_cast<uint32_t>(f.gate >> 32));
+      tstore(o + 4, tag, static_cast<uint32_t>(f.up));
+      tstore(o + 5, tag, static_cast<uint32_t>(f.up >> 32));
+      tstore(o + 6, tag, static_cast<uint32_t>(f.down));
+      tstore(o + 7, tag, static_cast<uint32_t>(f.down >> 32));
+    }
   }
 }
 
@@ -646,50 +877,48 @@ __device__ void select_row(const Args& a, int r, int* sel, float* wsel) {
 // kernels
 // ---------------------------------------------------------------------------
 // route: router workgroups [0, E) write logits; record builders
-// [E, E + kPrepWGs) build the activation records of every format.
+// [E, E + kPrepWGs) build the activation records of every format; in
+// moe_layer, the shared expert's gate/up tiles follow (they need only x, so
+// their weights stream while the router runs; records are built locally).
 template <class S>
 __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_route(Args a) {
-  __shared__ double red[kMaxRows * 16];
+  extern __shared__ __align__(16) uint8_t lds[];
   const int bid = blockIdx.x;
-  if (bid >= a.E) {
+  if (bid < a.E) {
+    __shared__ double red[kMaxRows * 16];
+    router_wg<S::kH>(a, bid, red);
+    return;
+  }
+  if (bid < a.E + kPrepWGs) {
     prep_wg<S>(a, bid - a.E);
     return;
   }
-  router_wg<S::kH>(a, bid, red);
-}
-
-__device__ void shared_entry_init(const Args& a, SlotEntry* e) {
+  __shared__ SlotEntry se;
+  const int tile = bid - a.E - kPrepWGs;
   if (threadIdx.x == 0) {
-    e->ref = *a.shared;
-    e->expert = -1;
-    e->nt = a.R;
+    se.ref = *a.shared;
+    se.expert = -1;
+    se.nt = a.R;
     for (int r = 0; r < a.R; ++r) {
-      e->row[r] = r;
-      e->pair[r] = a.R * a.k + r;
-      e->w[r] = 1.0f;
+      se.row[r] = r;
+      se.pair[r] = a.R * a.k + r;
+      se.w[r] = 1.0f;
     }
   }
   __syncthreads();
+  if (tile < tiles_of<S, true>(se.ref.fmt)) run_slot<S, 2>(a, se, tile, lds);
 }
 
-// select: workgroup 0 picks the top-k per row and builds the slot table;
-// workgroups 1.. stream the shared expert's gate/up tiles meanwhile (they
-// depend only on x), so the selection's latency is hidden behind them.
+// select: one workgroup picks the top-k of every row and builds the slot
+// table and the work lists.
 template <class S>
-__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_select(Args a) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ SlotEntry se;
-  if (blockIdx.x > 0) {
-    shared_entry_init(a, &se);
-    run_slot<S, 1>(a, se, blockIdx.x - 1, lds);
-    return;
-  }
+__global__ __launch_bounds__(kThreads) void k_select(Args a) {
   __shared__ int sel[kMaxRows * kMaxK];
   __shared__ float wsel[kMaxRows * kMaxK];
   for (int r = threadIdx.x >> 6; r < a.R; r += blockDim.x >> 6)
     select_row(a, r, sel + r * a.k, wsel + r * a.k);
   __syncthreads();
-  if (a.experts && threadIdx.x < 64) build_slot_table(a, sel, wsel);
+  if (a.experts && threadIdx.x < 64) build_slot_table<S>(a, sel, wsel, a.slots, true);
 }
 
 // Preparation for a caller-given routing: slot table (workgroup 0) and
@@ -704,54 +933,187 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_prep(Args a) {
       wv[i] = a.wts[i];
     }
     __syncthreads();
-    if (threadIdx.x < 64) build_slot_table(a, ids, wv);
+    if (threadIdx.x < 64) build_slot_table<S>(a, ids, wv, a.slots, true);
     return;
   }
   prep_wg<S>(a, blockIdx.x - 1);
 }
 
-__device__ __forceinline__ void load_slot(const Args& a, int si, SlotEntry* sl) {
-  if (threadIdx.x < static_cast<int>(sizeof(SlotEntry) / 4))
-    reinterpret_cast<uint32_t*>(sl)[threadIdx.x] = reinterpret_cast<const uint32_t*>(&a.slots->e[si])[threadIdx.x];
+// Work items of one list, strided over `nw` workers (this is worker w): each
+// item finds its slot in the offsets (binary search over at most 65 slots),
+// copies the slot entry to LDS and runs the tile.  STAGE as in run_slot;
+// the list is the down list for STAGE 0, else the gate/up list.
+template <class S, int STAGE, bool TAG>
+__device__ __forceinline__ void run_items(const Args& a, const SlotTable* tab, int w, int nw, uint8_t* lds,
+                          uint32_t tag = 0) {
+  __shared__ SlotEntry sl;
+  __shared__ int offs[kMaxSlots + 2];
+  const int ns = uniform(tab->n_slots);
+  const int* off_g = STAGE == 0 ? tab->dn_off : tab->gu_off;
+  const int n_items = uniform(off_g[ns]);
+  if (w >= n_items) return;
+  for (int i = threadIdx.x; i <= ns; i += blockDim.x) offs[i] = off_g[i];
   __syncthreads();
+  for (int item = w; item < n_items; item += nw) {
+    int lo = 0, hi = ns - 1;           // largest slot with offs[slot] <= item
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (offs[mid] <= item) lo = mid;
+      else hi = mid - 1;
+    }
+    const int slot = lo, tile = item - offs[lo];
+    if (threadIdx.x < static_cast<int>(sizeof(SlotEntry) / 4))
+      reinterpret_cast<uint32_t*>(&sl)[threadIdx.x] =
+          reinterpret_cast<const uint32_t*>(&tab->e[slot])[threadIdx.x];
+    __syncthreads();
+    run_slot<S, STAGE, TAG>(a, sl, tile, lds, tag);
+    __syncthreads();                    // the slot entry and LDS are reused
+  }
 }
 
-// gateup: routed (slot, tile) workgroups [0, n_slots * TILES_GU); then the
-// shared expert's gate/up tiles (caller-given routing) or, in moe_layer, its
-// down tiles, which only need the shared h of the previous kernel.
+// gateup: h = silu(W_gate x) * (W_up x) for every (slot, tile) item.
 template <class S>
-__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_gateup(Args a, int n_slots) {
+__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_gateup(Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ SlotEntry sl;
-  const int routed = n_slots * S::TILES_GU;
-  if (static_cast<int>(blockIdx.x) >= routed) {
-    shared_entry_init(a, &sl);
-    if (a.shared_early) run_slot<S, 0>(a, sl, blockIdx.x - routed, lds);
-    else run_slot<S, 1>(a, sl, blockIdx.x - routed, lds);
-    return;
-  }
-  const int slot = blockIdx.x % n_slots, tile = blockIdx.x / n_slots;
-  if (slot >= a.slots->n_active) return;
-  load_slot(a, slot, &sl);
-  run_slot<S, 1>(a, sl, tile, lds);
+  run_items<S, 1, false>(a, a.slots, blockIdx.x, gridDim.x, lds);
 }
 
-// down: routed (slot, output tile) workgroups write w * (W_down h) into the
-// partials; then the shared expert's down tiles when not done earlier.
+// down: w * (W_down h) into the partials for every (slot, tile) item.
 template <class S>
-__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_down(Args a, int n_slots) {
+__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_down(Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
-  __shared__ SlotEntry sl;
-  const int routed = n_slots * S::TILES_DN;
-  if (static_cast<int>(blockIdx.x) >= routed) {
-    shared_entry_init(a, &sl);
-    run_slot<S, 0>(a, sl, blockIdx.x - routed, lds);
+  run_items<S, 0, false>(a, a.slots, blockIdx.x, gridDim.x, lds);
+}
+
+// ---------------------------------------------------------------------------
+// fused layer: one launch, workgroup roles in dependency order
+// ---------------------------------------------------------------------------
+// [0, E)              router GEMV, logits published as tagged words
+// [E, E + R)          selection of row blockIdx - E (one wave), published tagged
+// [E + R, base_b)     the shared expert's gate/up tiles (need only x)
+// [base_b, base_c)    gate/up workers over the routed (slot, tile) items
+// [base_c, +nc)       down workers over the routed and shared items
+// Every role waits only on roles with lower workgroup ids, which the
+// dispatcher has started before it, so the waits always end; the workers
+// build the slot table themselves from the published selection.  Down
+// workers issue their weight loads before they wait for h.
+template <class S>
+__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int bid = blockIdx.x;
+  // this call's tag; nothing writes epoch[0] during the launch, so every
+  // workgroup reads the same value (the load's latency overlaps the first work)
+  const uint32_t tag = *a.epoch + 1u;
+  if (bid < a.E) {
+    __shared__ double red[kMaxRows * 16];
+    if (bid == 0 && threadIdx.x == 0) a.epoch[1] = tag;   // read by the combine
+    router_wg<S::kH>(a, bid, red, tag);
     return;
   }
-  const int slot = blockIdx.x % n_slots, tile = blockIdx.x / n_slots;
-  if (slot >= a.slots->n_active) return;
-  load_slot(a, slot, &sl);
-  run_slot<S, 0>(a, sl, tile, lds);
+  if (bid < a.E + a.R) {
+    __shared__ int sel[kMaxK];
+    __shared__ float wsel[kMaxK];
+    // the expert table goes to LDS while the router still runs, so the
+    // published entries carry their matrices without another round trip
+    moe_expert_ref* refs = reinterpret_cast<moe_expert_ref*>(lds);
+    for (int i = threadIdx.x; i < a.E * 4; i += blockDim.x)
+      reinterpret_cast<uint64_t*>(refs)[i] = reinterpret_cast<const uint64_t*>(a.experts)[i];
+    __syncthreads();
+    if (threadIdx.x < 64) select_row_tagged(a, bid - a.E, sel, wsel, tag, refs);
+    return;
+  }
+  if (bid < a.base_b) {
+    __shared__ SlotEntry se;
+    if (threadIdx.x == 0) {
+      se.ref = *a.shared;
+      se.expert = -1;
+      se.nt = a.R;
+      for (int r = 0; r < a.R; ++r) {
+        se.row[r] = r;
+        se.pair[r] = a.R * a.k + r;
+        se.w[r] = 1.0f;
+      }
+    }
+    __syncthreads();
+    const int tile = bid - a.E - a.R;
+    if (tile < tiles_of<S, true>(se.ref.fmt)) run_slot<S, 2, true>(a, se, tile, lds, tag);
+    return;
+  }
+  // workers: the selection of every row, then the slot table in LDS
+  __shared__ SlotTable tab;
+  __shared__ int ids[kMaxRows * kMaxK];
+  __shared__ float wv[kMaxRows * kMaxK];
+  __shared__ uint32_t ew[kMaxRows * kMaxK * kSelWords];
+  const int n = a.R * a.k;
+  {
+    constexpr int PER = kMaxRows * kMaxK * kSelWords / kThreads;
+    uint32_t v[PER];
+    await_batch<PER>(
+        [selt = a.selt, lim = n * kSelWords](int j) -> const uint64_t* {
+          const int i = threadIdx.x + j * kThreads;
+          return i < lim ? selt + i : nullptr;
+        },
+        tag, a.err, v);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) ew[threadIdx.x + j * kThreads] = v[j];
+  }
+  __syncthreads();
+  __shared__ moe_expert_ref eref[kMaxRows * kMaxK];
+  if (threadIdx.x < n) {
+    const uint32_t* w = ew + threadIdx.x * kSelWords;
+    ids[threadIdx.x] = static_cast<int>(w[0] & 0xFFFFu);
+    wv[threadIdx.x] = __builtin_bit_cast(float, w[1]);
+    moe_expert_ref& f = eref[threadIdx.x];
+    f.fmt = w[0] >> 16;
+    f.reserved = 0;
+    f.gate = (static_cast<uint64_t>(w[3]) << 32) | w[2];
+    f.up = (static_cast<uint64_t>(w[5]) << 32) | w[4];
+    f.down = (static_cast<uint64_t>(w[7]) << 32) | w[6];
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref);
+  __syncthreads();
+  if (bid < a.base_c) run_items<S, 2, true>(a, &tab, bid - a.base_b, a.nb, lds, tag);
+  else run_items<S, 0, true>(a, &tab, bid - a.base_c, a.nc, lds, tag);
+}
+
+// Combine after the fused launch: the row's k partials in ascending expert id
+// (ids from the published selection), then the shared expert.  Advances the
+// workspace epoch.  A call in which a hand-off wait gave up yields NaN.
+template <class S>
+__global__ __launch_bounds__(kThreads) void k_combine_fused(Args a) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t tag = a.epoch[1];     // the fused call's tag, recorded by it
+  if (i == 0) a.epoch[0] = tag;        // the next fused call runs with tag + 1
+  if (i >= a.R * S::kH) return;
+  const int r = i / S::kH, n = i - r * S::kH;
+  // every load first, then the sum in ascending id order (rank of each entry)
+  int id[kMaxK], rank[kMaxK];
+  float v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    id[j] = j < a.k ? static_cast<int>(static_cast<uint32_t>(a.selt[kSelWords * (r * a.k + j)]) & 0xFFFFu)
+                    : 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    v[j] = j < a.k ? a.part[static_cast<size_t>(r * a.k + j) * S::kH + n] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rank[j] = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) rank[j] += id[q] < id[j];
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int pos = 0; pos < kMaxK; ++pos) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) t = rank[j] == pos ? v[j] : t;
+    if (pos < a.k) s += t;
+  }
+  if (a.shared) s += a.part[static_cast<size_t>(a.R * a.k + r) * S::kH + n];
+  if (*a.err == tag) s = __builtin_nanf("");
+  a.y[i] = s;
 }
 
 // Combine: y[r] = sum over the row's experts in ascending id, then the shared
@@ -776,7 +1138,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
 namespace {
 
 struct WsLayout {
-  size_t logits, idx, wts, slots, order, xinv, xrec, h, part, total;
+  size_t epoch, logits, idx, wts, slots, order, xinv, xrec, h, part, lgt, selt, ht, total;
   int xrow;
 };
 
@@ -792,6 +1154,7 @@ WsLayout ws_layout(const moe_dims& d, int rows) {
   size_t o = 0;
   const size_t pairs = static_cast<size_t>(rows) * d.top_k + rows;
   l.xrow = xrow_for(d);
+  l.epoch = o;    o = align_up(o + 16, 256);   // epoch[2], err: at offset 0 for every row count
   l.logits = o;   o = align_up(o + 8 * static_cast<size_t>(rows) * d.n_experts, 256);
   l.idx = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
   l.wts = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
@@ -801,6 +1164,9 @@ WsLayout ws_layout(const moe_dims& d, int rows) {
   l.xrec = o;     o = align_up(o + static_cast<size_t>(dev::kNumFmt) * rows * l.xrow, 256);
   l.h = o;        o = align_up(o + 4 * pairs * d.inter, 256);
   l.part = o;     o = align_up(o + 4 * pairs * d.hidden, 256);
+  l.lgt = o;      o = align_up(o + 16 * static_cast<size_t>(rows) * d.n_experts, 256);
+  l.selt = o;     o = align_up(o + 8 * dev::kSelWords * static_cast<size_t>(rows) * d.top_k, 256);
+  l.ht = o;       o = align_up(o + 8 * pairs * d.inter, 256);
   l.total = o;
   return l;
 }
@@ -822,6 +1188,45 @@ int check_dims(const moe_dims* d, int rows) {
   return MOE_OK;
 }
 
+
+// Grid of a work-list launch: enough workgroups for every item of the
+// heaviest format mix, capped (items beyond the grid are strided over).
+constexpr int kMaxGrid = 1024;
+int item_grid(int upper) { return upper < kMaxGrid ? upper : kMaxGrid; }
+
+// moe_layer: the fused launch, then the combine.
+template <class S>
+int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const WsLayout& l,
+                 hipStream_t s, void* const* events, int n_events) {
+  const int n_routed = rows * d->top_k;
+  const bool sh = a.shared != nullptr;
+  a.epoch = reinterpret_cast<uint32_t*>(w8 + l.epoch);
+  a.err = a.epoch + 2;
+  a.lgt = reinterpret_cast<uint64_t*>(w8 + l.lgt);
+  a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
+  a.ht = reinterpret_cast<uint64_t*>(w8 + l.ht);
+  a.shared_early = 1;                       // the shared gate/up has its own workgroups
+  a.base_b = d->n_experts + rows + (sh ? S::MAX_TILES_GU : 0);
+  a.nb = item_grid(n_routed * S::MAX_TILES_GU);
+  a.base_c = a.base_b + a.nb;
+  a.nc = item_grid((n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN);
+  const size_t lds = S::LDS_WITH_STAGE;
+  int ev = 0;
+  auto rec = [&]() {
+    if (events && ev < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[ev]), s);
+    ++ev;
+  };
+  rec();
+  hipLaunchKernelGGL(dev::k_layer<S>, dim3(a.base_c + a.nc), dim3(dev::kThreads), lds, s, a);
+  rec();
+  if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
+  hipLaunchKernelGGL(dev::k_combine_fused<S>, dim3((rows * S::kH + dev::kThreads - 1) / dev::kThreads),
+                     dim3(dev::kThreads), 0, s, a);
+  rec();
+  if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
+  return MOE_OK;
+}
+
 template <class S>
 int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn, hipStream_t s,
                  void* const* events, int n_events) {
@@ -839,24 +1244,24 @@ int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn,
   };
   rec();
   if (route) {
-    hipLaunchKernelGGL(dev::k_route<S>, dim3(d->n_experts + dev::kPrepWGs), dim3(dev::kThreads), 0,
-                       s, a);
+    const int shared_gu = (sh && a.shared_early) ? S::MAX_TILES_GU : 0;
+    hipLaunchKernelGGL(dev::k_route<S>, dim3(d->n_experts + dev::kPrepWGs + shared_gu),
+                       dim3(dev::kThreads), S::LDS_WITH_STAGE, s, a);
     if (!launched()) return MOE_EDEVICE;
-    const int shared_gu = (sh && a.shared_early) ? S::TILES_GU : 0;
-    hipLaunchKernelGGL(dev::k_select<S>, dim3(1 + shared_gu), dim3(dev::kThreads), lds, s, a);
+    hipLaunchKernelGGL(dev::k_select<S>, dim3(1), dim3(dev::kThreads), 0, s, a);
     if (!launched()) return MOE_EDEVICE;
   } else {
     hipLaunchKernelGGL(dev::k_prep<S>, dim3(1 + dev::kPrepWGs), dim3(dev::kThreads), 0, s, a);
     if (!launched()) return MOE_EDEVICE;
   }
   if (ffn) {
-    const int shared_b = sh ? (a.shared_early ? S::TILES_DN : S::TILES_GU) : 0;
-    hipLaunchKernelGGL(dev::k_gateup<S>, dim3(n_routed * S::TILES_GU + shared_b), dim3(dev::kThreads),
-                       lds, s, a, n_routed);
+    const int slots_gu = n_routed + ((sh && !a.shared_early) ? 1 : 0);
+    const int slots_dn = n_routed + (sh ? 1 : 0);
+    hipLaunchKernelGGL(dev::k_gateup<S>, dim3(item_grid(slots_gu * S::MAX_TILES_GU)),
+                       dim3(dev::kThreads), lds, s, a);
     if (!launched()) return MOE_EDEVICE;
-    const int shared_c = (sh && !a.shared_early) ? S::TILES_DN : 0;
-    hipLaunchKernelGGL(dev::k_down<S>, dim3(n_routed * S::TILES_DN + shared_c), dim3(dev::kThreads),
-                       lds, s, a, n_routed);
+    hipLaunchKernelGGL(dev::k_down<S>, dim3(item_grid(slots_dn * S::MAX_TILES_DN)),
+                       dim3(dev::kThreads), lds, s, a);
     if (!launched()) return MOE_EDEVICE;
     hipLaunchKernelGGL(dev::k_combine<S>, dim3((rows * S::kH + dev::kThreads - 1) / dev::kThreads),
                        dim3(dev::kThreads), 0, s, a);
@@ -902,6 +1307,13 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   a.E = d->n_experts;
   a.shared_early = (route && ffn && shared) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (route && ffn) {
+    switch (shape_class(d)) {
+      case 1: return launch_fused<dev::Shape<5120, 2304>>(d, rows, a, w8, l, s, events, n_events);
+      case 2: return launch_fused<dev::Shape<512, 256>>(d, rows, a, w8, l, s, events, n_events);
+      default: return MOE_ESHAPE;
+    }
+  }
   switch (shape_class(d)) {
     case 1: return launch_layer<dev::Shape<5120, 2304>>(d, rows, a, route, ffn, s, events, n_events);
     case 2: return launch_layer<dev::Shape<512, 256>>(d, rows, a, route, ffn, s, events, n_events);
@@ -983,7 +1395,7 @@ int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        const moe_expert_ref* experts, const moe_expert_ref* shared,
                        int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes,
                        void* stream, void* const* events, int32_t n_events) {
-  if (!events || n_events < 6) return MOE_EINVAL;
+  if (!events || n_events < 3) return MOE_EINVAL;
   return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y,
                   ws, ws_bytes, stream, true, true, events, n_events);
 }

@@ -164,9 +164,10 @@ int moe_check_experts(const moe_dims* dims, const moe_expert_ref* table, int32_t
  *   idx      [rows x top_k] int32, device, out: selected ids, key desc / id asc
  *   wts      [rows x top_k] fp32, device, out: mixing weights (unbiased softmax
  *            renormalised over the selection)
- *   ws       device workspace of ws_bytes >= moe_workspace_bytes(dims, rows);
- *            its contents need no initialisation.  One workspace must not
- *            serve two calls that can overlap.
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(dims, rows).
+ *            Zero-fill it once before its first use by any entry point;
+ *            every call leaves it valid for the next, for any row count.
+ *            One workspace must not serve two calls that can overlap.
  * rows == 0 returns MOE_OK and launches nothing. */
 int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, int32_t* idx, float* wts, void* ws, size_t ws_bytes,
@@ -186,19 +187,22 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
                    void* stream);
 
-/* The whole layer: moe_route followed by moe_expert_ffn, with the shared
- * expert's gate/up streamed concurrently with the router.  idx and wts are
- * outputs as in moe_route. */
+/* The whole layer, same results as moe_route followed by moe_expert_ffn, in
+ * two launches: one fused launch whose workgroups hand logits, selections and
+ * h to each other inside the launch (router, selection, shared-expert
+ * gate/up, routed gate/up, down), then the fixed-order combine.  The shared
+ * expert and the down weights stream while their inputs are still being
+ * computed.  idx and wts are outputs as in moe_route.  Should a hand-off
+ * inside the fused launch ever fail to arrive, its waits end after a bounded
+ * spin and y is filled with NaN. */
 int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, const void* weights, const moe_expert_ref* experts,
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
               size_t ws_bytes, void* stream);
 
-/* moe_layer with timing: `events` holds n_events >= 6 hipEvent_t handles
- * created by the caller.  events[0] is recorded before the first kernel and
- * events[i] after the i-th of the layer's five kernels: (1) router GEMV,
- * activation records and shared-expert gate/up, (2) top-k selection,
- * (3) routed gate/up + SwiGLU, (4) down projections, (5) combine. */
+/* moe_layer with timing: `events` holds n_events >= 3 hipEvent_t handles
+ * created by the caller, recorded on the stream before the fused launch,
+ * after it, and after the combine. */
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        const float* w_router, const float* sel_bias, const void* weights,
                        const moe_expert_ref* experts, const moe_expert_ref* shared,

@@ -59,25 +59,28 @@ def test_tiny_repeated_rows_share_experts():
 
 
 def test_tiny_deterministic_and_workspace_reuse():
+    """One zero-filled workspace serves calls of different row counts in turn
+    (the fused launch's hand-off words are tagged per call, so words left by
+    earlier calls must never be taken); equal inputs give bitwise equal y."""
     wl = synth.WORKLOADS["tiny"]
     dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
     ys = []
     ws = LY.workspace(dl.dims, 8)
-    ws.fill_(0xA5)                                 # contents need no initialisation
-    for rep, stream in enumerate([10, 11, 10]):
-        xbits = synth.x_bf16(wl, 0, 8, stream)
+    for rows, stream in [(8, 10), (3, 11), (8, 12), (8, 10), (1, 13)]:
+        xbits = synth.x_bf16(wl, 0, rows, stream)
         xd = G.device_inputs(wl, 0, xbits)
-        idx = torch.zeros((8, 2), dtype=torch.int32, device="cuda")
-        wts = torch.zeros((8, 2), dtype=torch.float32, device="cuda")
-        y = torch.zeros((8, wl.hidden), dtype=torch.float32, device="cuda")
-        L.moe_layer(dl.dims, xd, 8, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
+        idx = torch.zeros((rows, 2), dtype=torch.int32, device="cuda")
+        wts = torch.zeros((rows, 2), dtype=torch.float32, device="cuda")
+        y = torch.zeros((rows, wl.hidden), dtype=torch.float32, device="cuda")
+        L.moe_layer(dl.dims, xd, rows, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
                     idx, wts, y, ws)
         torch.cuda.synchronize()
         ys.append(y.cpu().numpy())
         x, ri, rw, logits, gap = G.oracle_route(wl, 0, xbits)
         assert np.array_equal(idx.cpu().numpy(), ri)
-        assert np.all(G.rel_l2_rows(ys[-1], G.oracle_y(wl, 0, x, ri, rw, list(range(8)))) <= G.REL_L2_TOL)
-    assert np.array_equal(ys[0], ys[2])            # bitwise reproducible
+        ref = G.oracle_y(wl, 0, x, ri, rw, list(range(rows)))
+        assert np.all(G.rel_l2_rows(ys[-1], ref) <= G.REL_L2_TOL)
+    assert np.array_equal(ys[0], ys[3])            # bitwise reproducible
 
 
 def test_route_only_and_ffn_only_match_layer():
@@ -159,3 +162,27 @@ def test_expert_ffn_each_format_real_shape(fmt):
     err = G.rel_l2_rows(y.cpu().numpy(), ref)
     _say(f"  {fmt}: rel L2 per row", err)
     assert np.all(err <= G.REL_L2_TOL)
+
+
+def test_fused_layer_matches_split_calls_real_shape():
+    """moe_layer (fused launch) against moe_route + moe_expert_ffn (one launch
+    per step) on the mixed-format verify layer with 5 rows: same ids, same y."""
+    wl = synth.WORKLOADS["mixed_verify"]
+    rows = 5
+    xbits = synth.x_bf16(wl, 0, rows, 21)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    dl = LY.DeviceLayer(wl, 0, materialize=need)
+    xd = G.device_inputs(wl, 0, xbits)
+    gi, gw, gy, _ = G.run_layer(dl, xd, rows)
+    ws = LY.workspace(dl.dims, rows)
+    idx2 = torch.zeros((rows, wl.top_k), dtype=torch.int32, device="cuda")
+    wts2 = torch.zeros((rows, wl.top_k), dtype=torch.float32, device="cuda")
+    L.moe_route(dl.dims, xd, rows, dl.router, dl.bias, idx2, wts2, ws)
+    y2 = torch.zeros((rows, wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_expert_ffn(dl.dims, xd, rows, idx2, wts2, dl.weights, dl.experts, dl.shared, y2, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx2.cpu().numpy(), gi)
+    assert np.array_equal(wts2.cpu().numpy(), gw)
+    np.testing.assert_allclose(y2.cpu().numpy(), gy, rtol=1e-6, atol=1e-6)
+    G.check_routing(gi, gw, idx, w, gap, logits)
