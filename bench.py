@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--sweep", default="1,5,8", help="extra row counts reported beside the headline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=1)
+    p.add_argument("--copy-calib-mb", type=int, default=0,
+                   help="run one device copy of this many MiB first (a known-size reference "
+                        "for hardware byte counters)")
     return p.parse_args()
 
 
@@ -74,6 +77,23 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_k_layer_decode_q2_rows1.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter runs,
+    or None when the kernel sources changed since they were taken."""
+    from bit_moe_expert_02_amd import profile_summary
+    try:
+        with open(TRAFFIC_FILE) as f:
+            d = json.load(f)
+    except OSError:
+        return None
+    if d.get("source_sha256") != profile_summary.source_hash():
+        return None
+    return int(d["traffic_bytes_per_launch"])
 
 
 def layer_bytes(wl, fmts_unique, rows):
@@ -187,6 +207,13 @@ def main():
     print(f"[bench] building {args.copies} layer copies of {wl.name}", file=sys.stderr, flush=True)
     layers = build_copies(wl, args.copies, args.pool)
     torch.cuda.synchronize()
+    if args.copy_calib_mb:
+        src = torch.ones(args.copy_calib_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def xs_for(rows, n, base):
         return [torch.from_numpy(synth.x_bf16(wl, 0, rows, base + i).view(np.int16).copy()).cuda()
@@ -255,7 +282,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if args.rows == 1 else None,
             "kernel": "k_layer (fused router, selection, gate/up + SwiGLU, down)",
             "bytes_per_launch": int(fused_bytes),
             "avg_launch_us": round(b_ms * 1e3, 3),

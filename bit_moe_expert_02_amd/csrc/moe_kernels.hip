@@ -388,17 +388,22 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
     // records are built while the weights are still in flight and one round
     // trip to memory covers both
     constexpr int XCH = (H / 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread and row
-    uint4 xq[kNTB][XCH];
+    u32x4 xq[kNTB][XCH];
     if constexpr (STAGE_LOCAL) {
+      // buffer loads: chunks past the row or rows past the batch read an
+      // offset beyond the buffer and come back as zeros, without branches
+      const Buf xb = make_buf(reinterpret_cast<const uint8_t*>(a.x), static_cast<uint32_t>(a.R * H * 2));
+      constexpr uint32_t kNone = 0x7FFFFFF0u;
 #pragma unroll
-      for (int t = 0; t < kNTB; ++t)
+      for (int t = 0; t < kNTB; ++t) {
+        const int row = t < nb ? uniform(sl.row[t0 + t]) : 0;
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
           const int ch = threadIdx.x + i * kThreads;
-          xq[t][i] = (t < nb && ch < H / 8)
-                         ? *reinterpret_cast<const uint4*>(a.x + static_cast<size_t>(sl.row[t0 + t]) * H + 8 * ch)
-                         : uint4{0u, 0u, 0u, 0u};
+          const uint32_t off = (t < nb && ch < H / 8) ? static_cast<uint32_t>((row * H + 8 * ch) * 2) : kNone;
+          xq[t][i] = bload128(xb, off);
         }
+      }
     }
     st.load(0, mats, rows, I, valid);            // weights in flight while records are staged
     __syncthreads();
@@ -411,7 +416,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         for (int i = 0; i < XCH; ++i) {
           const int ch = threadIdx.x + i * kThreads;
           if (t < nb && ch < H / 8) {
-            *reinterpret_cast<uint4*>(xs + t * H + 8 * ch) = xq[t][i];
+            *reinterpret_cast<u32x4*>(xs + t * H + 8 * ch) = xq[t][i];
             const uint32_t w[4] = {xq[t][i].x, xq[t][i].y, xq[t][i].z, xq[t][i].w};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
