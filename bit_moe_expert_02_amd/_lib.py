@@ -23,7 +23,7 @@ MAX_TOP_K = 8
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
-           "moe_layer", "moe_layer_profiled")
+           "moe_layer", "moe_layer_profiled", "moe_stack_decode")
 
 
 class MoeError(RuntimeError):
@@ -35,6 +35,12 @@ class MoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [("w_router", ctypes.c_void_p), ("sel_bias", ctypes.c_void_p),
+                ("weights", ctypes.c_void_p), ("experts", ctypes.c_void_p),
+                ("shared", ctypes.c_void_p)]
 
 
 class ExpertRef(ctypes.Structure):
@@ -79,6 +85,9 @@ def lib():
         L.moe_layer_profiled.restype = ctypes.c_int
         L.moe_layer_profiled.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          vp, vp, i32]
+        L.moe_stack_decode.restype = ctypes.c_int
+        L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
+                                       vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -177,3 +186,20 @@ def moe_layer_profiled(d, x, rows, w_router, bias, weights, experts, shared, idx
         ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router), _ptr(bias), _ptr(weights),
         _ptr(experts), _ptr(shared), _ptr(idx), _ptr(wts), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream), arr, len(events)))
+
+
+def layer_weights(layers):
+    """ctypes array of LayerWeights for objects with router, bias, weights, experts, shared."""
+    arr = (LayerWeights * len(layers))()
+    for i, dl in enumerate(layers):
+        addr = [None if t is None else t.data_ptr()
+                for t in (dl.router, dl.bias, dl.weights, dl.experts, dl.shared)]
+        arr[i] = LayerWeights(*addr)
+    return arr
+
+
+def moe_stack_decode(d, layers, rows, x_all, noise, y_all, idx_all, wts_all, ws, stream=None):
+    """layers: a LayerWeights array (layer_weights()); the other buffers are torch tensors."""
+    _check("moe_stack_decode", lib().moe_stack_decode(
+        ctypes.byref(d), len(layers), layers, int(rows), _ptr(x_all), _ptr(noise), _ptr(y_all),
+        _ptr(idx_all), _ptr(wts_all), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

@@ -105,6 +105,9 @@ struct Args {
   uint64_t* selt;                 // [R x k x kSelWords] selection entries (see kSelWords)
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
   int base_b, nb, base_c, nc;     // gate/up and down worker ranges of the fused launch
+  // stack decode: the fused combine also writes the next layer's input
+  const float* noise;             // [R x H] fp32 added to y before rounding, or null
+  uint16_t* x_next;               // [R x H] bf16 out, or null
   int shared_early;               // 1: the shared expert's gate/up runs beside the router
                                   // (moe_layer), so the gate/up launch skips it
 };
@@ -1119,6 +1122,12 @@ __global__ __launch_bounds__(kThreads) void k_combine_fused(Args a) {
   if (a.shared) s += a.part[static_cast<size_t>(a.R * a.k + r) * S::kH + n];
   if (*a.err == tag) s = __builtin_nanf("");
   a.y[i] = s;
+  if (a.x_next) {   // stack decode: x_{l+1} = bf16 (round to nearest even) of the fp32 y + noise
+    const float v = a.noise ? s + a.noise[i] : s;
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
+    a.x_next[i] = static_cast<uint16_t>(u >> 16);
+  }
 }
 
 // Combine: y[r] = sum over the row's experts in ascending id, then the shared
@@ -1275,10 +1284,16 @@ int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn,
   return MOE_OK;
 }
 
+// Chained stack decode: where the fused combine writes the next layer's input.
+struct Chain {
+  const float* noise;
+  uint16_t* x_next;
+};
+
 int run(const moe_dims* d, const void* x, int rows, const float* w_router, const float* bias,
         const void* weights, const moe_expert_ref* experts, const moe_expert_ref* shared,
         int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes, void* stream,
-        bool route, bool ffn, void* const* events, int n_events) {
+        bool route, bool ffn, void* const* events, int n_events, const Chain* chain = nullptr) {
   int st = check_dims(d, rows);
   if (st) return st;
   if (rows == 0) return MOE_OK;
@@ -1311,6 +1326,10 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   a.k = d->top_k;
   a.E = d->n_experts;
   a.shared_early = (route && ffn && shared) ? 1 : 0;
+  if (chain) {
+    a.noise = chain->noise;
+    a.x_next = chain->x_next;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (route && ffn) {
     switch (shape_class(d)) {
@@ -1403,6 +1422,30 @@ int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
   if (!events || n_events < 3) return MOE_EINVAL;
   return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y,
                   ws, ws_bytes, stream, true, true, events, n_events);
+}
+
+int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_weights* layers,
+                     int32_t rows, void* x_all, const float* noise, float* y_all, int32_t* idx_all,
+                     float* wts_all, void* ws, size_t ws_bytes, void* stream) {
+  if (n_layers < 0 || (n_layers > 0 && (!layers || !x_all || !y_all))) return MOE_EINVAL;
+  if (int st = moe::check_dims(dims, rows)) return st;
+  const size_t xy = static_cast<size_t>(rows) * dims->hidden;
+  const size_t ik = static_cast<size_t>(rows) * dims->top_k;
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights& w = layers[l];
+    if (!w.w_router || !w.weights || !w.experts) return MOE_EINVAL;
+  }
+  uint16_t* x = static_cast<uint16_t*>(x_all);
+  for (int l = 0; l < n_layers; ++l) {
+    const moe_layer_weights& w = layers[l];
+    moe::Chain c{noise ? noise + l * xy : nullptr, x + (l + 1) * xy};
+    const int st = moe::run(dims, x + l * xy, rows, w.w_router, w.sel_bias, w.weights, w.experts,
+                            w.shared, idx_all ? idx_all + l * ik : nullptr,
+                            wts_all ? wts_all + l * ik : nullptr, y_all + l * xy, ws, ws_bytes,
+                            stream, true, true, nullptr, 0, &c);
+    if (st) return st;
+  }
+  return MOE_OK;
 }
 
 }  // extern "C"

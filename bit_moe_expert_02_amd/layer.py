@@ -64,14 +64,19 @@ class DeviceLayer:
             raise L.MoeError("moe_check_experts", st)
         self.weights = torch.zeros(total, dtype=torch.uint8, device=device)
         self.materialized = set()
+        # where each routed slot's weights come from: (layer, expert) for
+        # synth.expert_weights, or None for an all-zero expert
+        self.source = [None] * wl.n_experts
         for e in sorted(set(int(v) for v in materialize)):
             self._put(e, *self.pack_expert(e))
             self.materialized.add(e)
+            self.source[e] = (layer, e)
         if pool is not None:
             for e in range(wl.n_experts):
                 if e not in self.materialized:
                     p = pool[self.fmts[e]]
                     self._put_dev(e, p[e % len(p)])
+                    self.source[e] = (pool_layer(layer_of_pool(pool), self.fmts[e]), e % len(p))
         if wl.shared_fmt is not None:
             self._put(-1, *self.pack_expert(wl.n_experts))
         self.experts = torch.from_numpy(table.view(np.uint8).copy()).to(device)
@@ -105,14 +110,32 @@ class DeviceLayer:
             self.weights[int(off):int(off) + buf.numel()].copy_(buf)
 
 
+def pool_layer(layer, fmt):
+    """The synth layer key a pool's experts of `fmt` are drawn with."""
+    return layer + 1000 * (1 + list(L.FMT).index(fmt))
+
+
+class Pool(dict):
+    """fmt -> list of packed expert triples (device tensors); remembers its base layer."""
+
+    def __init__(self, layer):
+        super().__init__()
+        self.layer = layer
+
+
+def layer_of_pool(pool):
+    return getattr(pool, "layer", 0)
+
+
 def make_pool(wl, layer, fmts, count, device="cuda"):
-    """Distinct packed experts per format (device tensors), for throughput-only slots."""
+    """Distinct packed experts per format (device tensors), for throughput-only slots.
+    Item i of format f is synth.expert_weights(wl, pool_layer(layer, f), i), packed."""
     import torch
-    pool = {}
+    pool = Pool(layer)
     for f in sorted(set(fmts)):
         items = []
         for i in range(count):
-            g, u, d = synth.expert_weights(wl, layer + 1000 * (1 + list(L.FMT).index(f)), i)
+            g, u, d = synth.expert_weights(wl, pool_layer(layer, f), i)
             items.append(tuple(torch.from_numpy(L.pack(f, m)).to(device) for m in (g, u, d)))
         pool[f] = items
     return pool

@@ -57,6 +57,9 @@ WORKLOADS = {
     # 40-layer routed stack in the mixed formats
     "stack40_mixed": Workload("stack40_mixed", 4, 5120, 2304, 384, 6, "MIX", "Q8",
                               use_bias=True, layers=40, rows=(1, 7)),
+    # tiny stack in the mixed formats, CPU-checkable: chained decode parity
+    "tiny_stack": Workload("tiny_stack", 6, 512, 256, 16, 2, "MIX", "Q8", use_bias=True,
+                           layers=4, rows=(1, 7)),
     # 20-layer FP4 stack (no shared expert); 2048 rows is the prefill shape
     "fp4_stack20": Workload("fp4_stack20", 5, 5120, 2304, 384, 6, "MXFP4", None,
                             layers=20, rows=(1, 8, 2048)),

@@ -209,6 +209,36 @@ int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes,
                        void* stream, void* const* events, int32_t n_events);
 
+/* ------------------------------------------------------------------------ */
+/* Stack decode.                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* The device buffers of one layer, as passed to moe_layer. */
+typedef struct {
+  const float* w_router;          /* [E x H] fp32                          */
+  const float* sel_bias;          /* [E] fp32, or NULL                     */
+  const void* weights;            /* packed matrices                       */
+  const moe_expert_ref* experts;  /* [E] device                            */
+  const moe_expert_ref* shared;   /* [1] device, or NULL                   */
+} moe_layer_weights;
+
+/* Decode rows through a stack of layers, each layer's output (plus noise)
+ * feeding the next, as in the stacked-layer decode workloads:
+ *     y_l     = moe_layer(layer l, x_l)
+ *     x_{l+1} = bf16(y_l + noise_l)   (fp32 sum, then round to nearest even)
+ *   layers   host array of n_layers layer descriptions (device pointers)
+ *   x_all    [(n_layers + 1) x rows x H] bf16, device: the caller fills
+ *            x_all[0]; the call writes x_all[1 .. n_layers]
+ *   noise    [n_layers x rows x H] fp32, device, or NULL (no noise)
+ *   y_all    [n_layers x rows x H] fp32, device, out: every layer's y
+ *   idx_all, wts_all  [n_layers x rows x top_k], device, or NULL
+ *   ws       as for moe_layer (one workspace serves every layer)
+ * Two launches per layer on `stream`, no host synchronisation.  Every layer
+ * has the shape in dims.  Returns the first failing layer's status. */
+int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_weights* layers,
+                     int32_t rows, void* x_all, const float* noise, float* y_all,
+                     int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -206,3 +206,35 @@ def quant_mxfp8(x):
     e = np.clip(e, 0, 254)
     s = np.ldexp(1.0, e - 127)[..., None]
     return (round_e4m3(blk / s) * s).reshape(r, k), e
+
+
+# ----------------------------------------------------------------------------
+# stacked decode
+# ----------------------------------------------------------------------------
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def round_bf16(v):
+    """fp64 values -> nearest bf16 value, ties to the even significand.
+
+    A bf16 keeps 8 significant bits: quantum 2^(e-7) for |v| in [2^e, 2^(e+1))
+    with e >= -126, the subnormal quantum 2^-133 below 2^-126.  A result past
+    the largest finite bf16 is infinite (IEEE round to nearest)."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = np.maximum(ex - 1, -126)
+    q = np.ldexp(1.0, e - 7)
+    r = np.rint(a / q) * q                  # a / q is exact; rint ties to even
+    r = np.where(r > BF16_MAX, np.inf, r)
+    return np.copysign(r, v)
+
+
+def chain_next(y, eps):
+    """The next layer's input in a stacked decode: bf16 of the fp32 sum y + eps.
+
+    y and eps are fp32; the sum is one IEEE fp32 addition, then rounded to
+    bf16 (the workload feeds each layer's output plus Gaussian noise to the
+    next layer).  Returns fp64 values."""
+    s = np.asarray(y, np.float32) + np.asarray(eps, np.float32)
+    return round_bf16(s.astype(np.float64))

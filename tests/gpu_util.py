@@ -73,3 +73,27 @@ def check_routing(idx_gpu, w_gpu, idx_ref, w_ref, gap, logits):
     assert np.all(gap > NEAR_TIE * scale), "near-tie in the selection keys: inputs are ambiguous"
     assert np.array_equal(idx_gpu, idx_ref)
     np.testing.assert_allclose(w_gpu, w_ref, rtol=W_RTOL, atol=0)
+
+
+def oracle_y_for(dl, x, idx, w, rows):
+    """Oracle y for the given rows of a device layer whose routed slots may come
+    from a pool: each slot's weights are regenerated from dl.source."""
+    wl = dl.wl
+    cache = {}
+
+    def ex(e):
+        if e not in cache:
+            if e == wl.n_experts:
+                cache[e] = oracle_expert(wl, dl.layer, e)
+            else:
+                src = dl.source[e]
+                assert src is not None, f"slot {e} of layer {dl.layer} holds no weights"
+                fmt = dl.fmts[e]
+                g, u, d = synth.expert_weights(wl, src[0], src[1])
+                cache[e] = (OF.decode(fmt, OF.pack(fmt, g), wl.inter, wl.hidden),
+                            OF.decode(fmt, OF.pack(fmt, u), wl.inter, wl.hidden),
+                            OF.decode(fmt, OF.pack(fmt, d), wl.hidden, wl.inter))
+        return cache[e]
+
+    shared = ex(wl.n_experts) if wl.shared_fmt is not None else None
+    return OM.combine(x[rows], idx[rows], w[rows], ex, shared)
