@@ -45,6 +45,10 @@ def parse():
     p.add_argument("--sweep", default="1,5,8", help="extra row counts reported beside the headline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=1)
+    p.add_argument("--workload", default="decode_q2",
+                   choices=["decode_q2", "stack40_mixed", "fp4_stack20"],
+                   help="decode_q2: the single-layer headline; the stacks time whole "
+                        "chained decode passes (moe_stack_decode) and print their own line")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="run one device copy of this many MiB first (a known-size reference "
                         "for hardware byte counters)")
@@ -60,6 +64,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -188,6 +193,72 @@ def cpu_baseline(wl, rows):
                        f"experts and the shared expert + fp64 math), {t:.2f} s, BLAS 1 thread")
 
 
+def bench_stack(args, torch, L, LY, synth):
+    """Chained decode passes through a whole stack (every layer resident in HBM)."""
+    wl = synth.WORKLOADS[args.workload]
+    fmts = sorted({f for l in range(wl.layers) for f in synth.format_map(wl, l)})
+    print(f"[bench] building {wl.layers} layers of {wl.name} (pool of {args.pool} per format)",
+          file=sys.stderr, flush=True)
+    pool = LY.make_pool(wl, 0, fmts, args.pool)
+    layers = []
+    for l in range(wl.layers):
+        layers.append(LY.DeviceLayer(wl, l, materialize=(), pool=pool))
+        print(f"[bench]   layer {l} resident", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    lw = L.layer_weights(layers)
+    hev = HipEvents()
+    out_rows = {}
+    for rows in [r for r in wl.rows if r <= 8]:
+        H, k, n = wl.hidden, wl.top_k, wl.layers
+        x_all = torch.zeros((n + 1, rows, H), dtype=torch.int16, device="cuda")
+        noise = torch.from_numpy(np.stack([synth.noise(wl, l, rows) for l in range(n)])).cuda()
+        y_all = torch.zeros((n, rows, H), dtype=torch.float32, device="cuda")
+        idx_all = torch.zeros((n, rows, k), dtype=torch.int32, device="cuda")
+        ws = LY.workspace(layers[0].dims, rows)
+        x0 = [torch.from_numpy(synth.x_bf16(wl, 0, rows, 50_000 + i).view(np.int16).copy()).cuda()
+              for i in range(args.steps + args.warmup)]
+        ev = hev.create(2)
+        times, uniq_bytes = [], []
+        for i in range(args.steps + args.warmup):
+            x_all[0].copy_(x0[i])
+            if i >= args.warmup:
+                hev.hip.hipEventRecord(ctypes.c_void_p(ev[0]), None)
+            L.moe_stack_decode(layers[0].dims, lw, rows, x_all, noise, y_all, idx_all, None, ws)
+            if i >= args.warmup:
+                hev.hip.hipEventRecord(ctypes.c_void_p(ev[1]), None)
+                torch.cuda.synchronize()
+                times.append(hev.ms(ev[0], ev[1]))
+                ids = idx_all.cpu().numpy()
+                b = 0
+                for l in range(n):
+                    fm = layers[l].fmts
+                    b += layer_bytes(wl, [fm[e] for e in np.unique(ids[l])], rows)[0]
+                uniq_bytes.append(b)
+        hev.destroy(ev)
+        ms = float(np.mean(times))
+        gbps = float(np.mean(uniq_bytes)) / (ms * 1e-3) / 1e9
+        out_rows[rows] = dict(ms_per_pass=round(ms, 4), tokens_per_s=round(rows / (ms * 1e-3), 2),
+                              pass_bytes=int(np.mean(uniq_bytes)), GBps=round(gbps, 1),
+                              frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+        print(f"[bench] {wl.name} rows {rows}: {ms:.3f} ms/pass, {gbps:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    r0 = min(out_rows)
+    line = {
+        "metric": f"{wl.name} chained decode tokens/s (one pass = {wl.layers} layers)",
+        "value": out_rows[r0]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": out_rows[r0]["ms_per_pass"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "low-bit codes x f16 -> f32 (router f64)",
+        "data": "synthetic (seeded; unselected slots filled from a pool of distinct packed experts)",
+        "config": {"workload": wl.name, "layers": wl.layers, "rows": out_rows},
+        "roofline": {"bound": "hbm", "achieved": out_rows[r0]["GBps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": out_rows[r0]["frac_of_hbm_peak"], "traffic": None,
+                     "kernel": "whole pass (fused layer + combine per layer)"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -202,6 +273,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the MI355X"
     L.lib()
+    if args.workload != "decode_q2":
+        bench_stack(args, torch, L, LY, synth)
+        return
     wl = synth.WORKLOADS["decode_q2"]
     hev = HipEvents()
     print(f"[bench] building {args.copies} layer copies of {wl.name}", file=sys.stderr, flush=True)
