@@ -23,7 +23,7 @@ MAX_TOP_K = 8
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
-           "moe_layer", "moe_layer_profiled", "moe_stack_decode")
+           "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8")
 
 
 class MoeError(RuntimeError):
@@ -85,6 +85,8 @@ def lib():
         L.moe_layer_profiled.restype = ctypes.c_int
         L.moe_layer_profiled.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          vp, vp, i32]
+        L.moe_quant_mxfp8.restype = ctypes.c_int
+        L.moe_quant_mxfp8.argtypes = [vp, i32, i32, vp, vp, vp]
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
@@ -203,3 +205,8 @@ def moe_stack_decode(d, layers, rows, x_all, noise, y_all, idx_all, wts_all, ws,
     _check("moe_stack_decode", lib().moe_stack_decode(
         ctypes.byref(d), len(layers), layers, int(rows), _ptr(x_all), _ptr(noise), _ptr(y_all),
         _ptr(idx_all), _ptr(wts_all), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_quant_mxfp8(x, rows, k, codes, scales, stream=None):
+    _check("moe_quant_mxfp8", lib().moe_quant_mxfp8(_ptr(x), int(rows), int(k), _ptr(codes),
+                                                    _ptr(scales), _stream(stream)))

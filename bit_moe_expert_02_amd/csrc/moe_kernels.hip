@@ -34,6 +34,7 @@
 #include "dev_common.h"
 #include "formats_dev.h"
 #include "host_common.h"
+#include "prefill.h"
 
 namespace moe {
 namespace dev {
@@ -1241,6 +1242,14 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   return MOE_OK;
 }
 
+int check_prefill_dims(const moe_dims* d, int rows) {
+  if (!d) return MOE_EINVAL;
+  if (!shape_class(d)) return MOE_ESHAPE;
+  if (d->top_k < 1 || d->top_k > MOE_MAX_TOP_K || d->n_experts < d->top_k) return MOE_ESHAPE;
+  if (rows > MOE_MAX_PREFILL_ROWS) return MOE_ESHAPE;
+  return MOE_OK;
+}
+
 template <class S>
 int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn, hipStream_t s,
                  void* const* events, int n_events) {
@@ -1364,8 +1373,17 @@ const char* moe_status_string(int status) {
 }
 
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows) {
+  if (rows > MOE_MAX_DECODE_ROWS) {
+    if (moe::check_prefill_dims(dims, rows)) return 0;
+    return moe::pf::workspace_bytes(*dims, rows);
+  }
   if (moe::check_dims(dims, rows < 1 ? 1 : rows)) return 0;
   return moe::ws_layout(*dims, rows < 1 ? 1 : rows).total;
+}
+
+int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, void* scales,
+                    void* stream) {
+  return moe::pf::quant(x_bf16, rows, k, codes, scales, stream);
 }
 
 int moe_check_experts(const moe_dims* dims, const moe_expert_ref* table, int32_t count,
@@ -1401,6 +1419,11 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
                    const float* wts, const void* weights, const moe_expert_ref* experts,
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
                    void* stream) {
+  if (rows > MOE_MAX_DECODE_ROWS) {
+    if (int st = moe::check_prefill_dims(dims, rows)) return st;
+    return moe::pf::run(dims, x_bf16, rows, idx, wts, weights, experts, shared, y, ws, ws_bytes,
+                        stream);
+  }
   return moe::run(dims, x_bf16, rows, nullptr, nullptr, weights, experts, shared,
                   const_cast<int32_t*>(idx), const_cast<float*>(wts), y, ws, ws_bytes, stream,
                   false, true, nullptr, 0);

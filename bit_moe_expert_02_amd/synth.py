@@ -125,6 +125,24 @@ def format_map(wl, layer):
     return [names[i] for i in perm]
 
 
+def zipf_routing(wl, layer, rows, s=1.1, stream=0):
+    """Prefill routing given to the expert FFN: expert popularity p_i proportional
+    to rank_i^-s over a seeded permutation of the ids; each row takes the top_k
+    of log p + Gumbel noise (a draw of top_k distinct experts without
+    replacement), with weights = softmax of those keys over the selection.
+    Returns (idx int32 [rows x k], w fp32 [rows x k]), keys descending."""
+    g = rng(wl, layer, T_ROUTE, stream)
+    perm = g.permutation(wl.n_experts)
+    logp = np.empty(wl.n_experts)
+    logp[perm] = -s * np.log(np.arange(1, wl.n_experts + 1, dtype=np.float64))
+    keys = logp[None, :] + g.gumbel(size=(rows, wl.n_experts))
+    idx = np.argsort(-keys, axis=1, kind="stable")[:, :wl.top_k]
+    kv = np.take_along_axis(keys, idx, axis=1)
+    w = np.exp(kv - kv[:, :1])
+    w /= w.sum(axis=1, keepdims=True)
+    return idx.astype(np.int32), w.astype(np.float32)
+
+
 def noise(wl, layer, rows):
     """N(0,1) fp32 [rows x H] added to a layer's output before it feeds the next layer."""
     return rng(wl, layer, T_NOISE).standard_normal((rows, wl.hidden), dtype=np.float32)

@@ -84,6 +84,8 @@ typedef enum {
 #define MOE_MAX_DECODE_ROWS 8
 /* Largest top_k the selection kernel takes. */
 #define MOE_MAX_TOP_K 8
+/* Largest row count of moe_expert_ffn's many-row (prefill) path. */
+#define MOE_MAX_PREFILL_ROWS 8192
 
 const char* moe_status_string(int status);
 
@@ -173,6 +175,16 @@ int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const floa
               const float* sel_bias, int32_t* idx, float* wts, void* ws, size_t ws_bytes,
               void* stream);
 
+/* MXFP8 quantisation of activations (the prefill path's first step, exposed
+ * on its own): x [rows x k] bf16 (device) -> codes [rows x k] e4m3 and
+ * scales [rows x k/32] e8m0 (device).  Per 32 consecutive elements of a row:
+ * E = floor(log2 amax) - 8 + 127 clamped to [0, 254] (E = 0 for an all-zero
+ * block); element = e4m3 (OCP, finite-only variant) nearest to x / 2^(E-127),
+ * ties to the even significand, magnitudes at or above 448 saturating to 448.
+ * k must be a positive multiple of 32. */
+int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, void* scales,
+                    void* stream);
+
 /* Grouped expert FFN for a given routing.
  *   idx, wts   [rows x top_k], device, as produced by moe_route (any order of
  *              the k entries of a row is accepted; each row's ids must be
@@ -181,7 +193,14 @@ int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const floa
  *   experts    [n_experts] moe_expert_ref, device
  *   shared     [1] moe_expert_ref, device, or NULL (no shared expert)
  *   y          [rows x H] fp32, device, out (overwritten)
- * Deterministic: the same inputs give bitwise the same y. */
+ * Deterministic: the same inputs give bitwise the same y.
+ * rows <= MOE_MAX_DECODE_ROWS: the decode path, any formats.
+ * MOE_MAX_DECODE_ROWS < rows <= MOE_MAX_PREFILL_ROWS: the prefill path on the
+ * scaled matrix cores.  x and h = silu(W_gate x) * (W_up x) are quantised to
+ * MXFP8 (as moe_quant_mxfp8) before their products; every selected expert
+ * must be MXFP4 (a row that selects another format comes out NaN); shared
+ * must be NULL (else MOE_ESHAPE).  The workspace is moe_workspace_bytes(dims,
+ * rows) (about rows * top_k * (hidden * 4 + inter) bytes). */
 int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const int32_t* idx,
                    const float* wts, const void* weights, const moe_expert_ref* experts,
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,

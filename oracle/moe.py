@@ -209,6 +209,25 @@ def quant_mxfp8(x):
 
 
 # ----------------------------------------------------------------------------
+# prefill (many rows, MXFP4 experts on scaled matrix cores)
+# ----------------------------------------------------------------------------
+def prefill_layer(x, idx, w, expert_fn):
+    """y[r] = sum over the row's experts in ascending id of w * FFN_e(Q(x_r)),
+    Q = MXFP8 of the bf16 activations (the matrix cores take them as fp8),
+    FFN_e the SwiGLU expert in fp64 (h is not re-quantised).  x fp64 [R x H]
+    (exact bf16 values); expert_fn(e) -> decoded (gate, up, down)."""
+    x = np.asarray(x, np.float64)
+    xq, _ = quant_mxfp8(x)
+    y = np.zeros_like(x)
+    idx = np.asarray(idx)
+    for e in sorted(set(idx.reshape(-1).tolist())):
+        rows, cols = np.nonzero(idx == e)
+        o = expert_ffn(xq[rows], *expert_fn(e))
+        y[rows] += np.asarray(w, np.float64)[rows, cols][:, None] * o
+    return y
+
+
+# ----------------------------------------------------------------------------
 # stacked decode
 # ----------------------------------------------------------------------------
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127

@@ -215,3 +215,16 @@ def test_bf16_decode_exact():
     assert v[0] == 1.0 and v[1] == -1.0 and v[2] == 0.0
     assert v[4] == 3.140625
     assert v[5] == (2 - 2 ** -7) * 2.0 ** 127
+
+
+def test_zipf_routing_input_shape_and_skew():
+    """The prefill routing input: distinct ids per row, weights summing to 1,
+    popularity falling with rank (the most popular expert far above the mean)."""
+    from bit_moe_expert_02_amd import synth
+    wl = synth.WORKLOADS["fp4_stack20"]
+    idx, w = synth.zipf_routing(wl, 0, 2048)
+    assert idx.shape == (2048, 6) and w.shape == (2048, 6)
+    assert all(len(set(r)) == 6 for r in idx.tolist())
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
+    counts = np.bincount(idx.reshape(-1), minlength=384)
+    assert counts.max() > 20 * counts.mean() and counts.mean() == 32

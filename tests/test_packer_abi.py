@@ -104,7 +104,11 @@ def test_workspace_and_dims_validation(L):
     d = L.dims(5120, 2304, 384, 6)
     ws = L.workspace_bytes(d, 8)
     assert ws > 0 and ws % 256 == 0
-    assert L.workspace_bytes(d, 9) == 0                   # above the decode row limit
+    # above the decode row limit: the prefill path's workspace, which holds
+    # MXFP8 x, the dispatch, MXFP8 h and the fp32 per-pair partials
+    wp = L.workspace_bytes(d, 2048)
+    assert wp >= 2048 * 6 * (5120 * 4 + 2304) + 2048 * 5120 and wp % 256 == 0
+    assert L.workspace_bytes(d, 8193) == 0                # above the prefill row limit
     assert L.workspace_bytes(L.dims(4096, 2304, 384, 6), 1) == 0
     assert L.workspace_bytes(L.dims(5120, 2304, 384, 9), 1) == 0
     assert L.workspace_bytes(L.dims(512, 256, 16, 2), 4) > 0
