@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=1)
     p.add_argument("--workload", default="decode_q2",
-                   choices=["decode_q2", "stack40_mixed", "fp4_stack20"],
+                   choices=["decode_q2", "stack40_mixed", "fp4_stack20", "fp4_prefill"],
                    help="decode_q2: the single-layer headline; the stacks time whole "
                         "chained decode passes (moe_stack_decode) and print their own line")
     p.add_argument("--copy-calib-mb", type=int, default=0,
@@ -193,6 +193,60 @@ def cpu_baseline(wl, rows):
                        f"experts and the shared expert + fp64 math), {t:.2f} s, BLAS 1 thread")
 
 
+def bench_prefill(args, torch, L, LY, synth):
+    """One FP4 layer at the prefill shape: 2048 Zipf-routed rows through
+    moe_expert_ffn (MXFP8 x MXFP4 gate/up and f16 x MXFP4 down on the matrix cores)."""
+    wl = synth.WORKLOADS["fp4_stack20"]
+    R = 2048
+    copies = 2
+    pool = LY.make_pool(wl, 0, ["MXFP4"], args.pool)
+    layers = [LY.DeviceLayer(wl, c, materialize=(), pool=pool) for c in range(copies)]
+    idx, w = synth.zipf_routing(wl, 0, R)
+    used = np.unique(idx)
+    per = 3 * L.packed_bytes("MXFP4", wl.inter, wl.hidden)
+    wbytes = len(used) * per
+    flops = 2.0 * 3 * wl.hidden * wl.inter * R * wl.top_k
+    xs = [torch.from_numpy(synth.x_bf16(wl, 0, R, 900 + i).view(np.int16).copy()).cuda() for i in range(2)]
+    it, wt = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda()
+    y = torch.zeros((R, wl.hidden), dtype=torch.float32, device="cuda")
+    ws = LY.workspace(layers[0].dims, R)
+    hev = HipEvents()
+    ev = hev.create(2)
+    for i in range(args.warmup):
+        dl = layers[i % copies]
+        L.moe_expert_ffn(dl.dims, xs[i % 2], R, it, wt, dl.weights, dl.experts, None, y, ws)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(args.steps):
+        dl = layers[i % copies]
+        hev.hip.hipEventRecord(ctypes.c_void_p(ev[0]), None)
+        L.moe_expert_ffn(dl.dims, xs[i % 2], R, it, wt, dl.weights, dl.experts, None, y, ws)
+        hev.hip.hipEventRecord(ctypes.c_void_p(ev[1]), None)
+        torch.cuda.synchronize()
+        times.append(hev.ms(ev[0], ev[1]))
+    hev.destroy(ev)
+    ms = float(np.median(times))
+    gbps = wbytes / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] fp4 prefill {R} rows: {ms:.3f} ms/layer, {gbps:.0f} GB/s of expert weights, "
+          f"{tflops:.0f} TFLOP/s", file=sys.stderr, flush=True)
+    line = {
+        "metric": "FP4 prefill-layer tokens/s (2048 Zipf-routed rows, MXFP4 experts on the matrix cores)",
+        "value": round(R / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8 x mxfp4 (gate/up), f16 x mxfp4 (down) -> f32",
+        "data": "synthetic (seeded; Zipf s=1.1 routing; experts filled from a pool of distinct packed experts)",
+        "config": {"workload": "fp4 prefill: hidden 5120, moe_intermediate 2304, 384 MXFP4 experts, "
+                               "top-6, 2048 rows", "experts_touched": int(len(used)),
+                   "weight_bytes": int(wbytes), "flop": flops, "TFLOPs": round(tflops, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "whole prefill call (quant, dispatch, gate/up, down, combine)"},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def bench_stack(args, torch, L, LY, synth):
     """Chained decode passes through a whole stack (every layer resident in HBM)."""
     wl = synth.WORKLOADS[args.workload]
@@ -273,6 +327,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the MI355X"
     L.lib()
+    if args.workload == "fp4_prefill":
+        bench_prefill(args, torch, L, LY, synth)
+        return
     if args.workload != "decode_q2":
         bench_stack(args, torch, L, LY, synth)
         return
