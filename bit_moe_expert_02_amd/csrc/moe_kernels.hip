@@ -41,11 +41,11 @@ namespace dev {
 
 constexpr int kThreads = 256;
 #ifndef MOE_WAVES_PER_EU
-#define MOE_WAVES_PER_EU 2  // occupancy floor: 2 waves per SIMD (<= 256 VGPRs)
+#define MOE_WAVES_PER_EU 3  // occupancy floor: 3 waves per SIMD (<= 168 VGPRs)
 #endif
 constexpr int kMaxRows = MOE_MAX_DECODE_ROWS;  // rows per call on the decode path
 constexpr int kMaxK = MOE_MAX_TOP_K;
-constexpr int kNTB = 2;                        // token rows staged in LDS at once
+constexpr int kNTB = 1;                        // token rows staged in LDS at once
 constexpr int kMaxSlots = 64;                  // distinct routed experts per call (rows * top_k)
 constexpr int kNumFmt = 5;                     // format tags 1..5
 constexpr int kPrepWGs = 16;                   // workgroups building activation records
