@@ -26,6 +26,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <type_traits>
@@ -99,9 +100,9 @@ struct Args {
   int R, k, E;
   // fused layer (one launch for route, select, gate/up and down): tagged
   // hand-off words and the layout of the workgroup roles
-  uint32_t* epoch;                // [2] epoch[0]: a fused call runs with tag epoch[0] + 1 and
-                                  // records it in epoch[1]; its combine copies it to epoch[0]
+  uint32_t tag;                   // this call's tag: unique in the process (never 0)
   uint32_t* err;                  // [1] the tag of a call in which a wait gave up
+  uint64_t* part_t;               // [(R*k + R) x H] partial outputs as tagged fp32
   uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
   uint64_t* selt;                 // [R x k x kSelWords] selection entries (see kSelWords)
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
@@ -111,6 +112,10 @@ struct Args {
   uint16_t* x_next;               // [R x H] bf16 out, or null
   int shared_early;               // 1: the shared expert's gate/up runs beside the router
                                   // (moe_layer), so the gate/up launch skips it
+  int shared_own_down;            // 1: the shared expert's down has its own workgroups
+                                  // (fused launch), so the down list skips it
+  int base_sd;                    // fused launch: first shared-down workgroup
+  int base_y;                     // fused launch: first combine workgroup
 };
 
 // ---------------------------------------------------------------------------
@@ -565,8 +570,11 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
         if (t < nb) {
           const float sc = inv_sigma[t] * sl.w[t0 + t];
 #pragma unroll
-          for (int q = 0; q < NPG; ++q)
-            a.part[static_cast<size_t>(sl.pair[t0 + t]) * H + n0 + q] = acc[q][t] * sc;
+          for (int q = 0; q < NPG; ++q) {
+            const size_t o = static_cast<size_t>(sl.pair[t0 + t]) * H + n0 + q;
+            if constexpr (TAG) tstore(a.part_t + o, tag, __builtin_bit_cast(uint32_t, acc[q][t] * sc));
+            else a.part[o] = acc[q][t] * sc;
+          }
         }
       }
     }
@@ -644,7 +652,7 @@ __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, 
       e.expert = -1;
       e.nt = a.R;
       tg[n_active] = a.shared_early ? 0 : tiles_of<S, true>(ref.fmt);
-      td[n_active] = tiles_of<S, false>(ref.fmt);
+      td[n_active] = a.shared_own_down ? 0 : tiles_of<S, false>(ref.fmt);
     }
     e.row[lane] = lane;
     e.pair[lane] = n + lane;
@@ -994,14 +1002,63 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_down(Args a) {
   run_items<S, 0, false>(a, a.slots, blockIdx.x, gridDim.x, lds);
 }
 
+// Output element i = (r, n) of the fused launch: the row's k partials in
+// ascending expert id (ids from the published selection), then the shared
+// expert; every input is a tagged word of this call.  In a stack decode it
+// also writes the next layer's input.  A call in which a hand-off wait gave
+// up yields NaN (as far as this element can tell).
+template <class S>
+__device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) {
+  if (i >= a.R * S::kH) return;
+  const int r = i / S::kH, n = i - r * S::kH;
+  const int k = a.k;
+  uint32_t w[2 * kMaxK + 1];
+  await_batch<2 * kMaxK + 1>(
+      [sel = a.selt, part = a.part_t, r, n, k, sh = a.shared != nullptr, R = a.R](int j) -> const uint64_t* {
+        if (j < kMaxK) return j < k ? sel + kSelWords * (r * k + j) : nullptr;
+        const int q = j - kMaxK;
+        if (q < k) return part + static_cast<size_t>(r * k + q) * S::kH + n;
+        return (q == kMaxK && sh) ? part + static_cast<size_t>(R * k + r) * S::kH + n : nullptr;
+      },
+      tag, a.err, w);
+  int id[kMaxK], rank[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) id[j] = j < k ? static_cast<int>(w[j] & 0xFFFFu) : 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    rank[j] = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxK; ++q) rank[j] += id[q] < id[j];
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int pos = 0; pos < kMaxK; ++pos) {
+    float t = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) t = rank[j] == pos ? __builtin_bit_cast(float, w[kMaxK + j]) : t;
+    if (pos < k) s += t;
+  }
+  if (a.shared) s += __builtin_bit_cast(float, w[2 * kMaxK]);
+  if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
+  a.y[i] = s;
+  if (a.x_next) {   // stack decode: x_{l+1} = bf16 (round to nearest even) of the fp32 y + noise
+    const float v = a.noise ? s + a.noise[i] : s;
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
+    a.x_next[i] = static_cast<uint16_t>(u >> 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fused layer: one launch, workgroup roles in dependency order
 // ---------------------------------------------------------------------------
 // [0, E)              router GEMV, logits published as tagged words
 // [E, E + R)          selection of row blockIdx - E (one wave), published tagged
-// [E + R, base_b)     the shared expert's gate/up tiles (need only x)
+// [E + R, base_sd)    the shared expert's gate/up tiles (need only x)
+// [base_sd, base_b)   the shared expert's down tiles (need only the shared h)
 // [base_b, base_c)    gate/up workers over the routed (slot, tile) items
-// [base_c, +nc)       down workers over the routed and shared items
+// [base_c, base_y)    down workers over the routed items
+// [base_y, ...)       combine: one output element per thread
 // Every role waits only on roles with lower workgroup ids, which the
 // dispatcher has started before it, so the waits always end; the workers
 // build the slot table themselves from the published selection.  Down
@@ -1010,12 +1067,9 @@ template <class S>
 __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   extern __shared__ __align__(16) uint8_t lds[];
   const int bid = blockIdx.x;
-  // this call's tag; nothing writes epoch[0] during the launch, so every
-  // workgroup reads the same value (the load's latency overlaps the first work)
-  const uint32_t tag = *a.epoch + 1u;
+  const uint32_t tag = a.tag;
   if (bid < a.E) {
     __shared__ double red[kMaxRows * 16];
-    if (bid == 0 && threadIdx.x == 0) a.epoch[1] = tag;   // read by the combine
     router_wg<S::kH>(a, bid, red, tag);
     return;
   }
@@ -1032,6 +1086,9 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     return;
   }
   if (bid < a.base_b) {
+    // shared expert: gate/up tiles [E + R, base_sd), then its down tiles
+    // [base_sd, base_b), which wait for the shared h only and stream while the
+    // selection is still being made
     __shared__ SlotEntry se;
     if (threadIdx.x == 0) {
       se.ref = *a.shared;
@@ -1044,8 +1101,17 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
       }
     }
     __syncthreads();
-    const int tile = bid - a.E - a.R;
-    if (tile < tiles_of<S, true>(se.ref.fmt)) run_slot<S, 2, true>(a, se, tile, lds, tag);
+    if (bid < a.base_sd) {
+      const int tile = bid - a.E - a.R;
+      if (tile < tiles_of<S, true>(se.ref.fmt)) run_slot<S, 2, true>(a, se, tile, lds, tag);
+    } else {
+      const int tile = bid - a.base_sd;
+      if (tile < tiles_of<S, false>(se.ref.fmt)) run_slot<S, 0, true>(a, se, tile, lds, tag);
+    }
+    return;
+  }
+  if (bid >= a.base_y) {
+    combine_out<S>(a, (bid - a.base_y) * kThreads + threadIdx.x, tag);
     return;
   }
   // workers: the selection of every row, then the slot table in LDS
@@ -1086,51 +1152,6 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   else run_items<S, 0, true>(a, &tab, bid - a.base_c, a.nc, lds, tag);
 }
 
-// Combine after the fused launch: the row's k partials in ascending expert id
-// (ids from the published selection), then the shared expert.  Advances the
-// workspace epoch.  A call in which a hand-off wait gave up yields NaN.
-template <class S>
-__global__ __launch_bounds__(kThreads) void k_combine_fused(Args a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t tag = a.epoch[1];     // the fused call's tag, recorded by it
-  if (i == 0) a.epoch[0] = tag;        // the next fused call runs with tag + 1
-  if (i >= a.R * S::kH) return;
-  const int r = i / S::kH, n = i - r * S::kH;
-  // every load first, then the sum in ascending id order (rank of each entry)
-  int id[kMaxK], rank[kMaxK];
-  float v[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    id[j] = j < a.k ? static_cast<int>(static_cast<uint32_t>(a.selt[kSelWords * (r * a.k + j)]) & 0xFFFFu)
-                    : 0x7fffffff;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j)
-    v[j] = j < a.k ? a.part[static_cast<size_t>(r * a.k + j) * S::kH + n] : 0.0f;
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    rank[j] = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxK; ++q) rank[j] += id[q] < id[j];
-  }
-  float s = 0.0f;
-#pragma unroll
-  for (int pos = 0; pos < kMaxK; ++pos) {
-    float t = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) t = rank[j] == pos ? v[j] : t;
-    if (pos < a.k) s += t;
-  }
-  if (a.shared) s += a.part[static_cast<size_t>(a.R * a.k + r) * S::kH + n];
-  if (*a.err == tag) s = __builtin_nanf("");
-  a.y[i] = s;
-  if (a.x_next) {   // stack decode: x_{l+1} = bf16 (round to nearest even) of the fp32 y + noise
-    const float v = a.noise ? s + a.noise[i] : s;
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
-    a.x_next[i] = static_cast<uint16_t>(u >> 16);
-  }
-}
-
 // Combine: y[r] = sum over the row's experts in ascending id, then the shared
 // expert -- a fixed order, so y is bitwise reproducible.
 template <class S>
@@ -1153,7 +1174,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
 namespace {
 
 struct WsLayout {
-  size_t epoch, logits, idx, wts, slots, order, xinv, xrec, h, part, lgt, selt, ht, total;
+  size_t err, logits, idx, wts, slots, order, xinv, xrec, h, part, lgt, selt, ht, part_t, total;
   int xrow;
 };
 
@@ -1169,7 +1190,7 @@ WsLayout ws_layout(const moe_dims& d, int rows) {
   size_t o = 0;
   const size_t pairs = static_cast<size_t>(rows) * d.top_k + rows;
   l.xrow = xrow_for(d);
-  l.epoch = o;    o = align_up(o + 16, 256);   // epoch[2], err: at offset 0 for every row count
+  l.err = o;      o = align_up(o + 16, 256);
   l.logits = o;   o = align_up(o + 8 * static_cast<size_t>(rows) * d.n_experts, 256);
   l.idx = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
   l.wts = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
@@ -1182,6 +1203,7 @@ WsLayout ws_layout(const moe_dims& d, int rows) {
   l.lgt = o;      o = align_up(o + 16 * static_cast<size_t>(rows) * d.n_experts, 256);
   l.selt = o;     o = align_up(o + 8 * dev::kSelWords * static_cast<size_t>(rows) * d.top_k, 256);
   l.ht = o;       o = align_up(o + 8 * pairs * d.inter, 256);
+  l.part_t = o;   o = align_up(o + 8 * pairs * d.hidden, 256);
   l.total = o;
   return l;
 }
@@ -1206,25 +1228,39 @@ int check_dims(const moe_dims* d, int rows) {
 
 // Grid of a work-list launch: enough workgroups for every item of the
 // heaviest format mix, capped (items beyond the grid are strided over).
-constexpr int kMaxGrid = 1024;
+constexpr int kMaxGrid = 768;   // one residency round: 3 workgroups x 256 CUs
 int item_grid(int upper) { return upper < kMaxGrid ? upper : kMaxGrid; }
 
-// moe_layer: the fused launch, then the combine.
+// Tags of fused calls: unique in the process, so no word a workspace holds
+// from an earlier call can carry the tag of a later one.
+std::atomic<uint32_t> g_call_tag{0};
+uint32_t next_tag() {
+  uint32_t t;
+  do t = g_call_tag.fetch_add(1, std::memory_order_relaxed) + 1; while (t == 0);
+  return t;
+}
+
+// moe_layer: one fused launch.
 template <class S>
 int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const WsLayout& l,
                  hipStream_t s, void* const* events, int n_events) {
   const int n_routed = rows * d->top_k;
   const bool sh = a.shared != nullptr;
-  a.epoch = reinterpret_cast<uint32_t*>(w8 + l.epoch);
-  a.err = a.epoch + 2;
+  a.tag = next_tag();
+  a.err = reinterpret_cast<uint32_t*>(w8 + l.err);
+  a.part_t = reinterpret_cast<uint64_t*>(w8 + l.part_t);
   a.lgt = reinterpret_cast<uint64_t*>(w8 + l.lgt);
   a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
   a.ht = reinterpret_cast<uint64_t*>(w8 + l.ht);
-  a.shared_early = 1;                       // the shared gate/up has its own workgroups
-  a.base_b = d->n_experts + rows + (sh ? S::MAX_TILES_GU : 0);
+  a.shared_early = 1;                       // the shared expert has its own workgroups
+  a.shared_own_down = 1;
+  a.base_sd = d->n_experts + rows + (sh ? S::MAX_TILES_GU : 0);
+  a.base_b = a.base_sd + (sh ? S::MAX_TILES_DN : 0);
   a.nb = item_grid(n_routed * S::MAX_TILES_GU);
   a.base_c = a.base_b + a.nb;
-  a.nc = item_grid((n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN);
+  a.nc = item_grid(n_routed * S::MAX_TILES_DN);
+  a.base_y = a.base_c + a.nc;
+  const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;
   const size_t lds = S::LDS_WITH_STAGE;
   int ev = 0;
   auto rec = [&]() {
@@ -1232,11 +1268,7 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
     ++ev;
   };
   rec();
-  hipLaunchKernelGGL(dev::k_layer<S>, dim3(a.base_c + a.nc), dim3(dev::kThreads), lds, s, a);
-  rec();
-  if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
-  hipLaunchKernelGGL(dev::k_combine_fused<S>, dim3((rows * S::kH + dev::kThreads - 1) / dev::kThreads),
-                     dim3(dev::kThreads), 0, s, a);
+  hipLaunchKernelGGL(dev::k_layer<S>, dim3(a.base_y + ny), dim3(dev::kThreads), lds, s, a);
   rec();
   if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
   return MOE_OK;
@@ -1442,7 +1474,7 @@ int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        const moe_expert_ref* experts, const moe_expert_ref* shared,
                        int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes,
                        void* stream, void* const* events, int32_t n_events) {
-  if (!events || n_events < 3) return MOE_EINVAL;
+  if (!events || n_events < 2) return MOE_EINVAL;
   return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y,
                   ws, ws_bytes, stream, true, true, events, n_events);
 }

@@ -48,8 +48,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device calls are
  *     asynchronous on it; nothing synchronises the host.  Device faults surface
  *     at the caller's next synchronisation.
- *   - The library keeps no mutable global state: calls on different streams
- *     with different workspaces may run concurrently.
+ *   - The library's only mutable global state is a thread-safe counter that
+ *     gives every moe_layer call a process-unique tag.  Calls on different
+ *     streams with different workspaces may run concurrently.
  */
 #ifndef BIT_MOE_H
 #define BIT_MOE_H
@@ -207,21 +208,20 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
                    void* stream);
 
 /* The whole layer, same results as moe_route followed by moe_expert_ffn, in
- * two launches: one fused launch whose workgroups hand logits, selections and
- * h to each other inside the launch (router, selection, shared-expert
- * gate/up, routed gate/up, down), then the fixed-order combine.  The shared
- * expert and the down weights stream while their inputs are still being
- * computed.  idx and wts are outputs as in moe_route.  Should a hand-off
- * inside the fused launch ever fail to arrive, its waits end after a bounded
- * spin and y is filled with NaN. */
+ * one launch whose workgroups hand logits, selections, h and partial outputs
+ * to each other through words tagged with the call's tag (router, selection,
+ * shared-expert gate/up and down, routed gate/up, routed down, fixed-order
+ * combine).  The shared expert and the down weights stream while their
+ * inputs are still being computed.  idx and wts are outputs as in moe_route.
+ * Should a hand-off ever fail to arrive, its waits end after a bounded spin
+ * and y comes out NaN. */
 int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, const void* weights, const moe_expert_ref* experts,
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
               size_t ws_bytes, void* stream);
 
-/* moe_layer with timing: `events` holds n_events >= 3 hipEvent_t handles
- * created by the caller, recorded on the stream before the fused launch,
- * after it, and after the combine. */
+/* moe_layer with timing: `events` holds n_events >= 2 hipEvent_t handles
+ * created by the caller, recorded on the stream before and after the launch. */
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
                        const float* w_router, const float* sel_bias, const void* weights,
                        const moe_expert_ref* experts, const moe_expert_ref* shared,
@@ -252,7 +252,7 @@ typedef struct {
  *   y_all    [n_layers x rows x H] fp32, device, out: every layer's y
  *   idx_all, wts_all  [n_layers x rows x top_k], device, or NULL
  *   ws       as for moe_layer (one workspace serves every layer)
- * Two launches per layer on `stream`, no host synchronisation.  Every layer
+ * One launch per layer on `stream`, no host synchronisation.  Every layer
  * has the shape in dims.  Returns the first failing layer's status. */
 int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_weights* layers,
                      int32_t rows, void* x_all, const float* noise, float* y_all,

@@ -135,12 +135,12 @@ def test_entry_points_reject_bad_args_on_host(L):
     assert lib.moe_expert_ffn(dp, fake, 1, fake, fake, None, fake, None, fake, fake, ws_need, None) == L.MOE_EINVAL
     # rows == 0 is a no-op
     assert lib.moe_layer(dp, fake, 0, fake, None, fake, fake, None, fake, fake, fake, fake, ws_need, None) == L.MOE_OK
-    # profiled needs three events
+    # profiled needs two events
     assert lib.moe_layer_profiled(dp, fake, 1, fake, None, fake, fake, None, fake, fake, fake, fake,
                                   ws_need, None, None, 0) == L.MOE_EINVAL
-    evs = (ctypes.c_void_p * 2)()
+    evs = (ctypes.c_void_p * 1)()
     assert lib.moe_layer_profiled(dp, fake, 1, fake, None, fake, fake, None, fake, fake, fake, fake,
-                                  ws_need, None, evs, 2) == L.MOE_EINVAL
+                                  ws_need, None, evs, 1) == L.MOE_EINVAL
 
 
 def test_check_experts(L):
