@@ -113,6 +113,17 @@ __device__ __forceinline__ uint32_t bload8(const Buf& b, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(b.r, off, 0, 0);
 }
 
+// The work-item id through an empty asm statement.  Values derived from it are
+// then computed where they are used: left to itself, the compiler hoists every
+// lane-constant offset of every format's tile code to the kernel entry, where
+// they outlive the register cap and are spilled to scratch, and each reload
+// costs a memory round trip on the way to the weight loads.
+__device__ __forceinline__ int tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Wave-wide (64 lanes) sum of a double via cross-lane shuffles.
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -134,37 +145,34 @@ __device__ __forceinline__ double f64_from_order_key(uint64_t k) {
 __device__ __forceinline__ bool key_better(uint64_t ka, int ia, uint64_t kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
-template <int CTRL>
+// One arg-max step across lanes: the lane takes its DPP partner's (key, id)
+// when that is better (larger key, or the same key and a lower id).  Lanes of
+// rows left out by ROWMASK keep their own pair.  Branch-free.
+template <int CTRL, int ROWMASK>
 __device__ __forceinline__ void argmax_step(uint64_t& k, int& id) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k), CTRL, 0xF, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, static_cast<uint32_t>(k >> 32), CTRL, 0xF, 0xF, false);
-  const int oi = __builtin_amdgcn_update_dpp(0, id, CTRL, 0xF, 0xF, false);
+  const uint32_t klo = static_cast<uint32_t>(k), khi = static_cast<uint32_t>(k >> 32);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(klo, klo, CTRL, ROWMASK, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(khi, khi, CTRL, ROWMASK, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(id, id, CTRL, ROWMASK, 0xF, false);
   const uint64_t ok = (static_cast<uint64_t>(hi) << 32) | lo;
-  if (key_better(ok, oi, k, id)) {
-    k = ok;
-    id = oi;
-  }
+  const bool better = key_better(ok, oi, k, id);
+  k = better ? ok : k;
+  id = better ? oi : id;
 }
+// Wave-wide arg-max; every lane ends with the winner.  Four in-row steps
+// (quad swaps, half-row and row mirrors), then the row broadcasts of lanes 15
+// and 31 carry the rows' winners into row 3; lane 63 holds the wave's.
 __device__ __forceinline__ void wave_argmax(uint64_t& k, int& id) {
-  argmax_step<0xB1>(k, id);   // quad_perm [1,0,3,2]
-  argmax_step<0x4E>(k, id);   // quad_perm [2,3,0,1]
-  argmax_step<0x141>(k, id);  // row_half_mirror
-  argmax_step<0x140>(k, id);  // row_mirror: every lane holds its row's winner
-  uint64_t bk = 0;
-  int bi = 0x7fffffff;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(k), 16 * r);
-    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(k >> 32), 16 * r);
-    const int ri = __builtin_amdgcn_readlane(id, 16 * r);
-    const uint64_t rk = (static_cast<uint64_t>(hi) << 32) | lo;
-    if (r == 0 || key_better(rk, ri, bk, bi)) {
-      bk = rk;
-      bi = ri;
-    }
-  }
-  k = bk;
-  id = bi;
+  argmax_step<0xB1, 0xF>(k, id);    // quad_perm [1,0,3,2]
+  argmax_step<0x4E, 0xF>(k, id);    // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xF>(k, id);   // row_half_mirror
+  argmax_step<0x140, 0xF>(k, id);   // row_mirror: every lane holds its row's winner
+  argmax_step<0x142, 0xA>(k, id);   // row_bcast:15 into rows 1 and 3
+  argmax_step<0x143, 0xC>(k, id);   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(k), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(k >> 32), 63);
+  id = __builtin_amdgcn_readlane(id, 63);
+  k = (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

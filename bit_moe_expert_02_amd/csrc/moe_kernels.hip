@@ -42,7 +42,7 @@ namespace dev {
 
 constexpr int kThreads = 256;
 #ifndef MOE_WAVES_PER_EU
-#define MOE_WAVES_PER_EU 3  // occupancy floor: 3 waves per SIMD (<= 168 VGPRs)
+#define MOE_WAVES_PER_EU 4  // occupancy floor: 4 waves per SIMD (<= 128 VGPRs)
 #endif
 constexpr int kMaxRows = MOE_MAX_DECODE_ROWS;  // rows per call on the decode path
 constexpr int kMaxK = MOE_MAX_TOP_K;
@@ -190,6 +190,14 @@ struct Shape {
   // records, or h rows (fp32) handed over inside the fused launch
   static constexpr int LDS_STAGE = cmax(kNTB * I * 4, kNTB * H * 2);
   static constexpr int LDS_WITH_STAGE = LDS_BYTES + LDS_STAGE;
+  // fused launch: the workers' selection words, expert refs, ids and weights
+  // sit at the start of the dynamic region until the slot table is built
+  static constexpr int LDS_SEL_WORDS = kMaxRows * kMaxK * kSelWords * 4;
+  static constexpr int LDS_SEL = LDS_SEL_WORDS + kMaxRows * kMaxK * (static_cast<int>(sizeof(moe_expert_ref)) + 8);
+  // the selection workgroup keeps the whole expert table (up to 64 * kSelQ
+  // entries) there
+  static constexpr int LDS_REFS = 64 * kSelQ * static_cast<int>(sizeof(moe_expert_ref));
+  static constexpr int LDS_LAYER = cmax(cmax(LDS_WITH_STAGE, LDS_SEL), LDS_REFS);
 };
 
 // tiles of a format tag (device side: the tag comes from the expert table)
@@ -252,7 +260,7 @@ __device__ __forceinline__ uint32_t row_max_bits(const void* src, uint32_t* red)
   uint4 qs[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = threadIdx.x + i * kThreads;
+    const int c = tid() + i * kThreads;
     qs[i] = c < KR / PER ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
                                                            static_cast<size_t>(c) * 16)
                          : uint4{0, 0, 0, 0};
@@ -276,10 +284,10 @@ __device__ __forceinline__ uint32_t row_max_bits(const void* src, uint32_t* red)
   }
   m = wave_max_u32(m);
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  if ((tid() & 63) == 0) red[tid() >> 6] = m;
   __syncthreads();
   uint32_t r = 0;
-  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) r = r > red[w] ? r : red[w];
+  for (int w = 0; w < kThreads / 64; ++w) r = r > red[w] ? r : red[w];
   return r;
 }
 
@@ -331,7 +339,7 @@ struct Stream {
   }
   __device__ __forceinline__ void load(int p, const Buf (&mats)[RT],
                                        const int (&rows)[RT], int nrows, bool valid) {
-    const int c = threadIdx.x % LPR;
+    const int c = tid() % LPR;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int j = p * G + g;
@@ -344,7 +352,7 @@ struct Stream {
   __device__ __forceinline__ void run(const Buf (&mats)[RT], const int (&rows)[RT],
                                       int nrows, bool valid, const uint8_t* rec, int nt,
                                       float (&acc)[RT][NT], const uint32_t* table) {
-    const int c = threadIdx.x % LPR;
+    const int c = tid() % LPR;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       if (p + 1 < P) load(p + 1, mats, rows, nrows, valid);
@@ -362,7 +370,7 @@ struct Stream {
 template <class F>
 __device__ __forceinline__ void build_tern_table(uint32_t* table) {
   if constexpr (std::is_same_v<F, FmtTern>)
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) table[i] = FmtTern::table_entry(i);
+    for (int i = tid(); i < 256; i += kThreads) table[i] = FmtTern::table_entry(i);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,7 +390,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
   __shared__ uint32_t red[16];
   __shared__ const void* srcs[kNTB];
   build_tern_table<F>(table);
-  const int rg = threadIdx.x / LPR, c = threadIdx.x % LPR;
+  const int rg = tid() / LPR, c = tid() % LPR;
   const int n = tile * C::TN + rg;
   const bool valid = n < I;
   const Buf mats[2] = {make_buf(a.weights + sl.ref.gate, F::bytes(I, H)),
@@ -408,7 +416,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         const int row = t < nb ? uniform(sl.row[t0 + t]) : 0;
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
-          const int ch = threadIdx.x + i * kThreads;
+          const int ch = tid() + i * kThreads;
           const uint32_t off = (t < nb && ch < H / 8) ? static_cast<uint32_t>((row * H + 8 * ch) * 2) : kNone;
           xq[t][i] = bload128(xb, off);
         }
@@ -423,7 +431,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         uint32_t m = 0;
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
-          const int ch = threadIdx.x + i * kThreads;
+          const int ch = tid() + i * kThreads;
           if (t < nb && ch < H / 8) {
             *reinterpret_cast<u32x4*>(xs + t * H + 8 * ch) = xq[t][i];
             const uint32_t w[4] = {xq[t][i].x, xq[t][i].y, xq[t][i].z, xq[t][i].w};
@@ -436,11 +444,11 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
           }
         }
         m = wave_max_u32(m);
-        if ((threadIdx.x & 63) == 0) red[t * 4 + (threadIdx.x >> 6)] = m;
+        if ((tid() & 63) == 0) red[t * 4 + (tid() >> 6)] = m;
       }
       __syncthreads();
-      if (threadIdx.x < nb) {
-        const int t = threadIdx.x;
+      if (tid() < nb) {
+        const int t = tid();
         uint32_t m = 0;
         for (int w = 0; w < kThreads / 64; ++w) m = m > red[t * 4 + w] ? m : red[t * 4 + w];
         sig_exp[t] = sigma_exp<F>(m);
@@ -448,12 +456,12 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         srcs[t] = xs + t * H;
       }
       __syncthreads();
-      build_records<F, H, true>(srcs, nb, sig_exp, rec, threadIdx.x, blockDim.x);
+      build_records<F, H, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
     } else {
       // copy this format's records of the rows from the per-layer buffer
       // straight into LDS (global_load_lds_dwordx4): each wave moves 1 KB per
       // instruction, no registers involved
-      const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+      const int wave = tid() >> 6, lane = tid() & 63;
       constexpr int CHUNKS = RSTRIDE / 1024 + (RSTRIDE % 1024 ? 1 : 0);
       for (int t = 0; t < nb; ++t) {
         const uint8_t* src = a.xrec + (static_cast<size_t>(fi) * a.R + sl.row[t0 + t]) * a.xrow;
@@ -465,7 +473,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
                 (__attribute__((address_space(3))) void*)(rec + t * RSTRIDE + ch * 1024),
                 16, 0, 0);
         }
-        if (threadIdx.x == 0) inv_sigma[t] = a.xinv[fi * a.R + sl.row[t0 + t]];
+        if (tid() == 0) inv_sigma[t] = a.xinv[fi * a.R + sl.row[t0 + t]];
       }
     }
     __syncthreads();
@@ -503,7 +511,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
   __shared__ uint32_t red[16];
   __shared__ const void* srcs[kNTB];
   build_tern_table<F>(table);
-  const int rg = threadIdx.x / LPR, c = threadIdx.x % LPR;
+  const int rg = tid() / LPR, c = tid() % LPR;
   const int n0 = tile * C::TN + rg * NPG;
   const Buf md = make_buf(a.weights + sl.ref.down, F::bytes(H, I));
   Buf mats[NPG];
@@ -529,34 +537,34 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
         const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
         // first a sparse wait (one word in every I/kThreads, which samples
         // every gate/up tile of 16 channels), then the whole vector once
-        (void)await_word(src + (threadIdx.x * (I / kThreads)), tag, a.err);
+        (void)await_word(src + (tid() * (I / kThreads)), tag, a.err);
         uint32_t v[PER];
         await_batch<PER>(
             [src](int j) -> const uint64_t* {
-              const int i = threadIdx.x + j * kThreads;
+              const int i = tid() + j * kThreads;
               return i < I ? src + i : nullptr;
             },
             tag, a.err, v);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-          const int i = threadIdx.x + j * kThreads;
+          const int i = tid() + j * kThreads;
           if (i < I) hs[t * I + i] = __builtin_bit_cast(float, v[j]);
         }
       }
-      if (threadIdx.x < nb) srcs[threadIdx.x] = hs + threadIdx.x * I;
+      if (tid() < nb) srcs[tid()] = hs + tid() * I;
     } else {
-      if (threadIdx.x < nb) srcs[threadIdx.x] = a.h + static_cast<size_t>(sl.pair[t0 + threadIdx.x]) * I;
+      if (tid() < nb) srcs[tid()] = a.h + static_cast<size_t>(sl.pair[t0 + tid()]) * I;
     }
     __syncthreads();
     for (int t = 0; t < nb; ++t) {
       const uint32_t m = row_max_bits<I, false>(srcs[t], red);
-      if (threadIdx.x == 0) {
+      if (tid() == 0) {
         sig_exp[t] = sigma_exp<F>(m);
         inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
       }
     }
     __syncthreads();
-    build_records<F, I, false>(srcs, nb, sig_exp, rec, threadIdx.x, blockDim.x);
+    build_records<F, I, false>(srcs, nb, sig_exp, rec, tid(), kThreads);
     __syncthreads();
     float acc[NPG][kNTB] = {};
     st.template run<kNTB>(mats, rows, H, valid, rec, nb, acc, table);
@@ -613,7 +621,7 @@ template <class S>
 __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, const float* wv, SlotTable* tab,
                                  bool write_order, const moe_expert_ref* eref = nullptr) {
   __shared__ int tg[kMaxSlots + 1], td[kMaxSlots + 1];
-  const int lane = threadIdx.x;
+  const int lane = tid();
   const int n = a.R * a.k;
   const int v = lane < n ? ids[lane] : 0x7fffffff;
   bool first = lane < n;
@@ -694,17 +702,17 @@ __device__ __forceinline__ void prep_format(const Args& a, int p, const int* sig
   const int fi = F::TAG - 1;
   __shared__ int sig_exp[kMaxRows];
   __shared__ const void* srcs[kMaxRows];
-  if (threadIdx.x < a.R) {
-    sig_exp[threadIdx.x] = sig_base[threadIdx.x] - F::PSHIFT;
-    srcs[threadIdx.x] = a.x + static_cast<size_t>(threadIdx.x) * H;
-    if (p == 0) a.xinv[fi * a.R + threadIdx.x] = __builtin_ldexpf(1.0f, -sig_exp[threadIdx.x]);
+  if (tid() < a.R) {
+    sig_exp[tid()] = sig_base[tid()] - F::PSHIFT;
+    srcs[tid()] = a.x + static_cast<size_t>(tid()) * H;
+    if (p == 0) a.xinv[fi * a.R + tid()] = __builtin_ldexpf(1.0f, -sig_exp[tid()]);
   }
   __syncthreads();
   // rows of this format are a.xrow apart; build_records strides rows by the
   // format's own record row, so build one row at a time
   for (int r = 0; r < a.R; ++r)
     build_records<F, H, true>(srcs + r, 1, sig_exp + r, a.xrec + (static_cast<size_t>(fi) * a.R + r) * a.xrow,
-                              p * blockDim.x + threadIdx.x, kPrepWGs * blockDim.x);
+                              p * kThreads + tid(), kPrepWGs * kThreads);
 }
 
 template <class S>
@@ -713,7 +721,7 @@ __device__ __forceinline__ void prep_wg(const Args& a, int p) {
   __shared__ int base[kMaxRows];
   for (int r = 0; r < a.R; ++r) {
     const uint32_t m = row_max_bits<S::kH, true>(a.x + static_cast<size_t>(r) * S::kH, red);
-    if (threadIdx.x == 0) base[r] = m ? 14 - (static_cast<int>(m >> 23) - 127) : 14;
+    if (tid() == 0) base[r] = m ? 14 - (static_cast<int>(m >> 23) - 127) : 14;
   }
   __syncthreads();
   prep_format<S, FmtQ2>(a, p, base);
@@ -736,7 +744,7 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
   float4 w[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int j = threadIdx.x + i * kThreads;
+    const int j = tid() + i * kThreads;
     w[i] = j < H / 4 ? wr[j] : float4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
@@ -745,7 +753,7 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
       uint2 xb[CH];
 #pragma unroll
       for (int i = 0; i < CH; ++i) {
-        const int j = threadIdx.x + i * kThreads;
+        const int j = tid() + i * kThreads;
         xb[i] = j < H / 4 ? *reinterpret_cast<const uint2*>(a.x + static_cast<size_t>(r) * H + 4 * j)
                           : uint2{0u, 0u};
       }
@@ -760,7 +768,7 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
       acc[r] = s;
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = tid() >> 6, lane = tid() & 63, nw = kThreads / 64;
 #pragma unroll
   for (int r = 0; r < kMaxRows; ++r) {
     if (r < a.R) {
@@ -769,10 +777,10 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
     }
   }
   __syncthreads();
-  if (threadIdx.x < a.R) {
+  if (tid() < a.R) {
     double s = 0.0;
-    for (int w = 0; w < nw; ++w) s += red[threadIdx.x * 16 + w];
-    const size_t o = static_cast<size_t>(threadIdx.x) * a.E + e;
+    for (int w = 0; w < nw; ++w) s += red[tid() * 16 + w];
+    const size_t o = static_cast<size_t>(tid()) * a.E + e;
     if (a.lgt) {   // fused launch: publish as two tagged halves
       const uint64_t b = __builtin_bit_cast(uint64_t, s);
       tstore(a.lgt + 2 * o, tag, static_cast<uint32_t>(b));
@@ -786,11 +794,24 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
 // Top-k of one row by key = logit + bias, ties to the lower id; weights are
 // the softmax of the unbiased logits over the selection.  One wave per row;
 // the logits come from the previous kernel, so plain loads see them.
-__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ], int* sel, float* wsel,
-                            uint32_t tag, const moe_expert_ref* refs);
+__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ],
+                                           const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
+                                           const moe_expert_ref* refs);
+
+// The lane's share of the selection-only bias (0 where there is none).
+__device__ __forceinline__ void load_bias(const Args& a, float (&bias)[kSelQ]) {
+  const int lane = tid() & 63;
+#pragma unroll
+  for (int q = 0; q < kSelQ; ++q) {
+    const int e = lane + 64 * q;
+    bias[q] = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
+  }
+}
 
 __device__ __forceinline__ void select_row(const Args& a, int r, int* sel, float* wsel) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
+  float bias[kSelQ];
+  load_bias(a, bias);
   const double* lg = a.logits + static_cast<size_t>(r) * a.E;
   double lv[kSelQ];
 #pragma unroll
@@ -798,15 +819,17 @@ __device__ __forceinline__ void select_row(const Args& a, int r, int* sel, float
     const int e = lane + 64 * q;
     lv[q] = e < a.E ? lg[e] : 0.0;
   }
-  select_core(a, r, lv, sel, wsel, 0, nullptr);
+  select_core(a, r, lv, bias, sel, wsel, 0, nullptr);
 }
 
 // The fused launch: the row's logits arrive as tagged halves from the router
 // workgroups of the same launch.
 __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel, float* wsel, uint32_t tag,
                                   const moe_expert_ref* refs) {
-  const int lane = threadIdx.x & 63;
+  const int lane = tid() & 63;
   const uint64_t* lg = a.lgt + static_cast<size_t>(r) * a.E * 2;
+  float bias[kSelQ];   // loaded before the wait, off the critical path
+  load_bias(a, bias);
   uint32_t half[2 * kSelQ];
   await_batch<2 * kSelQ>(
       [lg, lane, E = a.E](int j) -> const uint64_t* {
@@ -818,57 +841,65 @@ __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q)
     lv[q] = __builtin_bit_cast(double, (static_cast<uint64_t>(half[2 * q + 1]) << 32) | half[2 * q]);
-  select_core(a, r, lv, sel, wsel, tag, refs);
+  select_core(a, r, lv, bias, sel, wsel, tag, refs);
 }
 
-__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ], int* sel, float* wsel,
-                            uint32_t tag, const moe_expert_ref* refs) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ],
+                                           const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
+                                           const moe_expert_ref* refs) {
+  const int lane = tid() & 63;
+  // selection keys as order-preserving integers; 0 (below every key) marks
+  // an empty slot
   uint64_t kv[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const int e = lane + 64 * q;
-    const double key = ((e < a.E && a.bias) ? lv[q] + static_cast<double>(a.bias[e]) : lv[q]) + 0.0;  // -0 -> +0
-    kv[q] = e < a.E ? f64_order_key(key) : 0ull;   // 0 is below every real key
+    const double key = (lv[q] + static_cast<double>(bias[q])) + 0.0;   // -0 -> +0
+    kv[q] = e < a.E ? f64_order_key(key) : 0ull;
   }
   double my_l = 0.0;     // lane j keeps the unbiased logit of the j-th selection
   int my_id = 0;
   double lmax = -INFINITY;
   for (int j = 0; j < a.k; ++j) {
-    uint64_t bk = 0;
-    int bid = 0x7fffffff;
-    double bl = 0.0;
+    // the lane's best: ids rise with q, so a strictly larger key is needed to
+    // move on (equal keys keep the lower id)
+    uint64_t bk = kv[0];
+    int bq = 0;
 #pragma unroll
-    for (int q = 0; q < kSelQ; ++q) {
-      const int e = lane + 64 * q;
-      if (e < a.E && key_better(kv[q], e, bk, bid)) {
-        bk = kv[q];
-        bid = e;
-        bl = lv[q];
-      }
+    for (int q = 1; q < kSelQ; ++q) {
+      const bool gt = kv[q] > bk;
+      bk = gt ? kv[q] : bk;
+      bq = gt ? q : bq;
     }
-    int wid = bid;
+    double bl = lv[0];
+#pragma unroll
+    for (int q = 1; q < kSelQ; ++q) bl = bq == q ? lv[q] : bl;
+    int wid = bk ? lane + 64 * bq : 0x7fffffff;
     uint64_t wk = bk;
     wave_argmax(wk, wid);
     // the winner's unbiased logit, from the lane that holds it
-    const int owner = wid & 63;
-    const uint32_t l_lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(__builtin_bit_cast(uint64_t, bl)), owner);
-    const uint32_t l_hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(__builtin_bit_cast(uint64_t, bl) >> 32), owner);
+    const int owner = wid & 63, wq = wid >> 6;
+    const uint64_t lb = __builtin_bit_cast(uint64_t, bl);
+    const uint32_t l_lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb), owner);
+    const uint32_t l_hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb >> 32), owner);
     const double wlog = __builtin_bit_cast(double, (static_cast<uint64_t>(l_hi) << 32) | l_lo);
 #pragma unroll
     for (int q = 0; q < kSelQ; ++q)
-      if (lane + 64 * q == wid) kv[q] = 0ull;   // taken
-    if (lane == j) {
-      my_l = wlog;
-      my_id = wid;
-    }
+      if (q == wq) kv[q] = lane == owner ? 0ull : kv[q];   // taken (q == wq is uniform)
+    my_l = lane == j ? wlog : my_l;
+    my_id = lane == j ? wid : my_id;
     lmax = wlog > lmax ? wlog : lmax;
   }
-  // softmax of the unbiased logits over the selection: one exp per lane
+  // softmax of the unbiased logits over the selection: one exp per lane, the
+  // sum gathered from the k lanes
   const double e = lane < a.k ? exp(my_l - lmax) : 0.0;
-  double s = e;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) s += __shfl_xor(s, o, 64);
+  double s = 0.0;
+  for (int j = 0; j < a.k; ++j) {
+    const uint64_t eb = __builtin_bit_cast(uint64_t, e);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(eb), j);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(eb >> 32), j);
+    s += __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+  }
   if (lane < a.k) {
     const float w = static_cast<float>(e / s);
     sel[lane] = my_id;
@@ -912,7 +943,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_route(Args a) {
   }
   __shared__ SlotEntry se;
   const int tile = bid - a.E - kPrepWGs;
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     se.ref = *a.shared;
     se.expert = -1;
     se.nt = a.R;
@@ -932,10 +963,10 @@ template <class S>
 __global__ __launch_bounds__(kThreads) void k_select(Args a) {
   __shared__ int sel[kMaxRows * kMaxK];
   __shared__ float wsel[kMaxRows * kMaxK];
-  for (int r = threadIdx.x >> 6; r < a.R; r += blockDim.x >> 6)
+  for (int r = tid() >> 6; r < a.R; r += kThreads / 64)
     select_row(a, r, sel + r * a.k, wsel + r * a.k);
   __syncthreads();
-  if (a.experts && threadIdx.x < 64) build_slot_table<S>(a, sel, wsel, a.slots, true);
+  if (a.experts && tid() < 64) build_slot_table<S>(a, sel, wsel, a.slots, true);
 }
 
 // Preparation for a caller-given routing: slot table (workgroup 0) and
@@ -945,12 +976,12 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_prep(Args a) {
   if (blockIdx.x == 0) {
     __shared__ int ids[kMaxRows * kMaxK];
     __shared__ float wv[kMaxRows * kMaxK];
-    for (int i = threadIdx.x; i < a.R * a.k; i += blockDim.x) {
+    for (int i = tid(); i < a.R * a.k; i += kThreads) {
       ids[i] = a.idx[i];
       wv[i] = a.wts[i];
     }
     __syncthreads();
-    if (threadIdx.x < 64) build_slot_table<S>(a, ids, wv, a.slots, true);
+    if (tid() < 64) build_slot_table<S>(a, ids, wv, a.slots, true);
     return;
   }
   prep_wg<S>(a, blockIdx.x - 1);
@@ -969,7 +1000,7 @@ __device__ __forceinline__ void run_items(const Args& a, const SlotTable* tab, i
   const int* off_g = STAGE == 0 ? tab->dn_off : tab->gu_off;
   const int n_items = uniform(off_g[ns]);
   if (w >= n_items) return;
-  for (int i = threadIdx.x; i <= ns; i += blockDim.x) offs[i] = off_g[i];
+  for (int i = tid(); i <= ns; i += kThreads) offs[i] = off_g[i];
   __syncthreads();
   for (int item = w; item < n_items; item += nw) {
     int lo = 0, hi = ns - 1;           // largest slot with offs[slot] <= item
@@ -979,9 +1010,9 @@ __device__ __forceinline__ void run_items(const Args& a, const SlotTable* tab, i
       else hi = mid - 1;
     }
     const int slot = lo, tile = item - offs[lo];
-    if (threadIdx.x < static_cast<int>(sizeof(SlotEntry) / 4))
-      reinterpret_cast<uint32_t*>(&sl)[threadIdx.x] =
-          reinterpret_cast<const uint32_t*>(&tab->e[slot])[threadIdx.x];
+    if (tid() < static_cast<int>(sizeof(SlotEntry) / 4))
+      reinterpret_cast<uint32_t*>(&sl)[tid()] =
+          reinterpret_cast<const uint32_t*>(&tab->e[slot])[tid()];
     __syncthreads();
     run_slot<S, STAGE, TAG>(a, sl, tile, lds, tag);
     __syncthreads();                    // the slot entry and LDS are reused
@@ -1078,11 +1109,14 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     __shared__ float wsel[kMaxK];
     // the expert table goes to LDS while the router still runs, so the
     // published entries carry their matrices without another round trip
+    // the selection is on every routed expert's critical path: its wave goes
+    // first among the waves sharing the SIMD
+    __builtin_amdgcn_s_setprio(3);
     moe_expert_ref* refs = reinterpret_cast<moe_expert_ref*>(lds);
-    for (int i = threadIdx.x; i < a.E * 4; i += blockDim.x)
+    for (int i = tid(); i < a.E * 4; i += kThreads)
       reinterpret_cast<uint64_t*>(refs)[i] = reinterpret_cast<const uint64_t*>(a.experts)[i];
     __syncthreads();
-    if (threadIdx.x < 64) select_row_tagged(a, bid - a.E, sel, wsel, tag, refs);
+    if (tid() < 64) select_row_tagged(a, bid - a.E, sel, wsel, tag, refs);
     return;
   }
   if (bid < a.base_b) {
@@ -1090,7 +1124,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     // [base_sd, base_b), which wait for the shared h only and stream while the
     // selection is still being made
     __shared__ SlotEntry se;
-    if (threadIdx.x == 0) {
+    if (tid() == 0) {
       se.ref = *a.shared;
       se.expert = -1;
       se.nt = a.R;
@@ -1111,34 +1145,40 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     return;
   }
   if (bid >= a.base_y) {
-    combine_out<S>(a, (bid - a.base_y) * kThreads + threadIdx.x, tag);
+    combine_out<S>(a, (bid - a.base_y) * kThreads + tid(), tag);
     return;
   }
-  // workers: the selection of every row, then the slot table in LDS
+  // workers: the selection of every row, then the slot table in LDS; the
+  // selection's staging shares the dynamic region with the tiles' records
   __shared__ SlotTable tab;
-  __shared__ int ids[kMaxRows * kMaxK];
-  __shared__ float wv[kMaxRows * kMaxK];
-  __shared__ uint32_t ew[kMaxRows * kMaxK * kSelWords];
+  uint32_t* ew = reinterpret_cast<uint32_t*>(lds);
+  moe_expert_ref* eref = reinterpret_cast<moe_expert_ref*>(lds + S::LDS_SEL_WORDS);
+  int* ids = reinterpret_cast<int*>(eref + kMaxRows * kMaxK);
+  float* wv = reinterpret_cast<float*>(ids + kMaxRows * kMaxK);
   const int n = a.R * a.k;
+  // every worker waits here: one lane polls one word until the selection
+  // shows up, so a thousand workgroups do not hammer the same lines, then the
+  // whole selection is read (and the words still missing are polled)
+  if (tid() == 0) (void)await_word(a.selt + n * kSelWords - 1, tag, a.err);
+  __syncthreads();
   {
     constexpr int PER = kMaxRows * kMaxK * kSelWords / kThreads;
     uint32_t v[PER];
     await_batch<PER>(
         [selt = a.selt, lim = n * kSelWords](int j) -> const uint64_t* {
-          const int i = threadIdx.x + j * kThreads;
+          const int i = tid() + j * kThreads;
           return i < lim ? selt + i : nullptr;
         },
         tag, a.err, v);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) ew[threadIdx.x + j * kThreads] = v[j];
+    for (int j = 0; j < PER; ++j) ew[tid() + j * kThreads] = v[j];
   }
   __syncthreads();
-  __shared__ moe_expert_ref eref[kMaxRows * kMaxK];
-  if (threadIdx.x < n) {
-    const uint32_t* w = ew + threadIdx.x * kSelWords;
-    ids[threadIdx.x] = static_cast<int>(w[0] & 0xFFFFu);
-    wv[threadIdx.x] = __builtin_bit_cast(float, w[1]);
-    moe_expert_ref& f = eref[threadIdx.x];
+  if (tid() < n) {
+    const uint32_t* w = ew + tid() * kSelWords;
+    ids[tid()] = static_cast<int>(w[0] & 0xFFFFu);
+    wv[tid()] = __builtin_bit_cast(float, w[1]);
+    moe_expert_ref& f = eref[tid()];
     f.fmt = w[0] >> 16;
     f.reserved = 0;
     f.gate = (static_cast<uint64_t>(w[3]) << 32) | w[2];
@@ -1146,7 +1186,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     f.down = (static_cast<uint64_t>(w[7]) << 32) | w[6];
   }
   __syncthreads();
-  if (threadIdx.x < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref);
+  if (tid() < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref);
   __syncthreads();
   if (bid < a.base_c) run_items<S, 2, true>(a, &tab, bid - a.base_b, a.nb, lds, tag);
   else run_items<S, 0, true>(a, &tab, bid - a.base_c, a.nc, lds, tag);
@@ -1156,7 +1196,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
 // expert -- a fixed order, so y is bitwise reproducible.
 template <class S>
 __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.x * kThreads + tid();
   if (i >= a.R * S::kH) return;
   const int r = i / S::kH, n = i - r * S::kH;
   float s = 0.0f;
@@ -1228,8 +1268,13 @@ int check_dims(const moe_dims* d, int rows) {
 
 // Grid of a work-list launch: enough workgroups for every item of the
 // heaviest format mix, capped (items beyond the grid are strided over).
-constexpr int kMaxGrid = 768;   // one residency round: 3 workgroups x 256 CUs
-int item_grid(int upper) { return upper < kMaxGrid ? upper : kMaxGrid; }
+// one residency round: MOE_WAVES_PER_EU workgroups of 4 waves per CU, 256 CUs
+constexpr int kMaxGrid = MOE_WAVES_PER_EU * 256;
+int item_grid(int upper, int cap = kMaxGrid) { return upper < cap ? upper : cap; }
+// Fused launch: gate/up and down workers (the down workers come after every
+// gate/up worker, so they take the slots the gate/up workers leave free).
+constexpr int kFusedGU = kMaxGrid;
+constexpr int kFusedDN = kMaxGrid;
 
 // Tags of fused calls: unique in the process, so no word a workspace holds
 // from an earlier call can carry the tag of a later one.
@@ -1256,12 +1301,12 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   a.shared_own_down = 1;
   a.base_sd = d->n_experts + rows + (sh ? S::MAX_TILES_GU : 0);
   a.base_b = a.base_sd + (sh ? S::MAX_TILES_DN : 0);
-  a.nb = item_grid(n_routed * S::MAX_TILES_GU);
+  a.nb = item_grid(n_routed * S::MAX_TILES_GU, kFusedGU);
   a.base_c = a.base_b + a.nb;
-  a.nc = item_grid(n_routed * S::MAX_TILES_DN);
+  a.nc = item_grid(n_routed * S::MAX_TILES_DN, kFusedDN);
   a.base_y = a.base_c + a.nc;
   const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;
-  const size_t lds = S::LDS_WITH_STAGE;
+  const size_t lds = S::LDS_LAYER;
   int ev = 0;
   auto rec = [&]() {
     if (events && ev < n_events) (void)hipEventRecord(static_cast<hipEvent_t>(events[ev]), s);

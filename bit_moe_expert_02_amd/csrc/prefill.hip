@@ -135,7 +135,7 @@ __device__ __forceinline__ int mx_quant32(const float (&v)[32], uint32_t (&q)[8]
 __global__ __launch_bounds__(kThreads) void k_quant(const uint16_t* x, int rows, int K, uint8_t* codes,
                                                     uint8_t* scales) {
   const int nb = K / 32;
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.x * kThreads + threadIdx.x;
   if (b >= rows * nb) return;
   const int r = b / nb, c = b - r * nb;
   const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<size_t>(r) * K + 32 * c);
@@ -503,7 +503,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
 // bitwise reproducible); an id outside [0, E) yields NaN.
 template <int H>
 __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= a.R * H) return;
   const int r = i / H, n = i - r * H;
   int id[MOE_MAX_TOP_K], rank[MOE_MAX_TOP_K];
