@@ -131,48 +131,31 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// Arg-max over the wave of (key, id): the larger key wins, equal keys go to
-// the lower id.  key is an order-preserving 64-bit image of a double.  DPP
-// inside each 16-lane row, then the four row winners through readlane.
-// Returns the winner in every lane.
-__device__ __forceinline__ uint64_t f64_order_key(double d) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, d);
-  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
-}
-__device__ __forceinline__ double f64_from_order_key(uint64_t k) {
-  return __builtin_bit_cast(double, (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k);
-}
-__device__ __forceinline__ bool key_better(uint64_t ka, int ia, uint64_t kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
-}
-// One arg-max step across lanes: the lane takes its DPP partner's (key, id)
-// when that is better (larger key, or the same key and a lower id).  Lanes of
-// rows left out by ROWMASK keep their own pair.  Branch-free.
+// A double moved across lanes by one DPP pattern; lanes of rows left out by
+// ROWMASK keep their own value.
 template <int CTRL, int ROWMASK>
-__device__ __forceinline__ void argmax_step(uint64_t& k, int& id) {
-  const uint32_t klo = static_cast<uint32_t>(k), khi = static_cast<uint32_t>(k >> 32);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(klo, klo, CTRL, ROWMASK, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(khi, khi, CTRL, ROWMASK, 0xF, false);
-  const int oi = __builtin_amdgcn_update_dpp(id, id, CTRL, ROWMASK, 0xF, false);
-  const uint64_t ok = (static_cast<uint64_t>(hi) << 32) | lo;
-  const bool better = key_better(ok, oi, k, id);
-  k = better ? ok : k;
-  id = better ? oi : id;
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32);
+  const uint32_t ol = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
+  const uint32_t oh = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(oh) << 32) | ol);
 }
-// Wave-wide arg-max; every lane ends with the winner.  Four in-row steps
-// (quad swaps, half-row and row mirrors), then the row broadcasts of lanes 15
-// and 31 carry the rows' winners into row 3; lane 63 holds the wave's.
-__device__ __forceinline__ void wave_argmax(uint64_t& k, int& id) {
-  argmax_step<0xB1, 0xF>(k, id);    // quad_perm [1,0,3,2]
-  argmax_step<0x4E, 0xF>(k, id);    // quad_perm [2,3,0,1]
-  argmax_step<0x141, 0xF>(k, id);   // row_half_mirror
-  argmax_step<0x140, 0xF>(k, id);   // row_mirror: every lane holds its row's winner
-  argmax_step<0x142, 0xA>(k, id);   // row_bcast:15 into rows 1 and 3
-  argmax_step<0x143, 0xC>(k, id);   // row_bcast:31 into rows 2 and 3
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(k), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(k >> 32), 63);
-  id = __builtin_amdgcn_readlane(id, 63);
-  k = (static_cast<uint64_t>(hi) << 32) | lo;
+// Wave-wide max of a double, NaN operands passed over; every lane gets it.
+// Four in-row steps (quad swaps, half-row and row mirrors), then the row
+// broadcasts of lanes 15 and 31 carry the rows' maxima into row 3, whose
+// lane 63 holds the wave's.
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = __builtin_fmax(v, dpp_f64<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
+  v = __builtin_fmax(v, dpp_f64<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
+  v = __builtin_fmax(v, dpp_f64<0x141, 0xF>(v));   // row_half_mirror
+  v = __builtin_fmax(v, dpp_f64<0x140, 0xF>(v));   // row_mirror
+  v = __builtin_fmax(v, dpp_f64<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+  v = __builtin_fmax(v, dpp_f64<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(b), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(b >> 32), 63);
+  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

@@ -54,6 +54,12 @@ constexpr int kSelQ = 8;                       // experts per lane in the select
 // A published selection entry of the fused launch, as tagged words: id | fmt << 16,
 // weight bits, then the gate, up and down offsets of the expert (low, high).
 constexpr int kSelWords = 8;
+// The fused launch publishes the selection in kSelRep copies, kSelRepWords
+// apart (separate lines and pages): the workers poll copy blockIdx % kSelRep,
+// so a thousand polling workgroups spread over many memory channels instead
+// of queueing on the same few lines.  Copy 0 is the one the combine reads.
+constexpr int kSelRep = 16;
+constexpr int kSelRepWords = kMaxRows * kMaxK * kSelWords;
 
 // One entry of the slot table: a distinct selected expert (or the shared one)
 // and the rows it serves.
@@ -104,7 +110,7 @@ struct Args {
   uint32_t* err;                  // [1] the tag of a call in which a wait gave up
   uint64_t* part_t;               // [(R*k + R) x H] partial outputs as tagged fp32
   uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
-  uint64_t* selt;                 // [R x k x kSelWords] selection entries (see kSelWords)
+  uint64_t* selt;                 // kSelRep copies of [R x k x kSelWords] selection entries
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
   int base_b, nb, base_c, nc;     // gate/up and down worker ranges of the fused launch
   // stack decode: the fused combine also writes the next layer's input
@@ -848,50 +854,59 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
                                            const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
                                            const moe_expert_ref* refs) {
   const int lane = tid() & 63;
-  // selection keys as order-preserving integers; 0 (below every key) marks
-  // an empty slot
-  uint64_t kv[kSelQ];
+  // selection keys as doubles: NaN marks an entry past E or already taken (the
+  // max instruction passes over NaN operands); a NaN key of a real expert
+  // becomes -inf so that it can still be chosen
+  double kd[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const int e = lane + 64 * q;
-    const double key = (lv[q] + static_cast<double>(bias[q])) + 0.0;   // -0 -> +0
-    kv[q] = e < a.E ? f64_order_key(key) : 0ull;
+    double key = (lv[q] + static_cast<double>(bias[q])) + 0.0;   // -0 -> +0
+    key = key == key ? key : -INFINITY;
+    kd[q] = e < a.E ? key : __builtin_nan("");
   }
-  double my_l = 0.0;     // lane j keeps the unbiased logit of the j-th selection
-  int my_id = 0;
-  double lmax = -INFINITY;
+  int my_id = 0;         // lane j ends with the j-th selection
   for (int j = 0; j < a.k; ++j) {
-    // the lane's best: ids rise with q, so a strictly larger key is needed to
-    // move on (equal keys keep the lower id)
-    uint64_t bk = kv[0];
-    int bq = 0;
+    double m = kd[0];
 #pragma unroll
-    for (int q = 1; q < kSelQ; ++q) {
-      const bool gt = kv[q] > bk;
-      bk = gt ? kv[q] : bk;
-      bq = gt ? q : bq;
+    for (int q = 1; q < kSelQ; ++q) m = __builtin_fmax(m, kd[q]);
+    m = wave_max_f64(m);
+    // the lowest id holding the maximum: the lowest q with a match, then the
+    // lowest lane of it (ids are lane + 64 q)
+    uint64_t bm = 0;
+    int wq = 0;
+#pragma unroll
+    for (int q = kSelQ - 1; q >= 0; --q) {
+      const uint64_t b = __ballot(kd[q] == m);
+      wq = b ? q : wq;
+      bm = b ? b : bm;
     }
-    double bl = lv[0];
-#pragma unroll
-    for (int q = 1; q < kSelQ; ++q) bl = bq == q ? lv[q] : bl;
-    int wid = bk ? lane + 64 * bq : 0x7fffffff;
-    uint64_t wk = bk;
-    wave_argmax(wk, wid);
-    // the winner's unbiased logit, from the lane that holds it
-    const int owner = wid & 63, wq = wid >> 6;
-    const uint64_t lb = __builtin_bit_cast(uint64_t, bl);
-    const uint32_t l_lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb), owner);
-    const uint32_t l_hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb >> 32), owner);
-    const double wlog = __builtin_bit_cast(double, (static_cast<uint64_t>(l_hi) << 32) | l_lo);
+    const int owner = static_cast<int>(__builtin_ctzll(bm));
 #pragma unroll
     for (int q = 0; q < kSelQ; ++q)
-      if (q == wq) kv[q] = lane == owner ? 0ull : kv[q];   // taken (q == wq is uniform)
-    my_l = lane == j ? wlog : my_l;
-    my_id = lane == j ? wid : my_id;
-    lmax = wlog > lmax ? wlog : lmax;
+      kd[q] = (q == wq && lane == owner) ? __builtin_nan("") : kd[q];   // taken
+    my_id = lane == j ? owner + 64 * wq : my_id;
   }
-  // softmax of the unbiased logits over the selection: one exp per lane, the
-  // sum gathered from the k lanes
+  // the unbiased logit of each lane's selection, fetched from the lane that
+  // holds it, then the softmax over the selection: one exp per lane, the max
+  // and the sum gathered from the k lanes
+  double my_l = 0.0;
+  {
+    const int oq = my_id >> 6, ol = my_id & 63;
+#pragma unroll
+    for (int q = 0; q < kSelQ; ++q) {
+      const double v = __shfl(lv[q], ol, 64);
+      my_l = oq == q ? v : my_l;
+    }
+  }
+  double lmax = -INFINITY;
+  for (int j = 0; j < a.k; ++j) {
+    const uint64_t lb = __builtin_bit_cast(uint64_t, my_l);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb), j);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(lb >> 32), j);
+    const double v = __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
+    lmax = v > lmax ? v : lmax;
+  }
   const double e = lane < a.k ? exp(my_l - lmax) : 0.0;
   double s = 0.0;
   for (int j = 0; j < a.k; ++j) {
@@ -900,23 +915,26 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(eb >> 32), j);
     s += __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
   }
+  const float w = static_cast<float>(e / s);
   if (lane < a.k) {
-    const float w = static_cast<float>(e / s);
     sel[lane] = my_id;
     wsel[lane] = w;
     a.idx[r * a.k + lane] = my_id;
     a.wts[r * a.k + lane] = w;
-    if (a.selt) {   // fused launch: publish the entry with its expert's matrices
-      uint64_t* o = a.selt + kSelWords * static_cast<size_t>(r * a.k + lane);
-      const moe_expert_ref& f = refs[my_id];
-      tstore(o, tag, static_cast<uint32_t>(my_id) | (f.fmt << 16));
-      tstore(o + 1, tag, __builtin_bit_cast(uint32_t, w));
-      tstore(o + 2, tag, static_cast<uint32_t>(f.gate));
-      tstore(o + 3, tag, static_cast<uint32_t>(f.gate >> 32));
-      tstore(o + 4, tag, static_cast<uint32_t>(f.up));
-      tstore(o + 5, tag, static_cast<uint32_t>(f.up >> 32));
-      tstore(o + 6, tag, static_cast<uint32_t>(f.down));
-      tstore(o + 7, tag, static_cast<uint32_t>(f.down >> 32));
+  }
+  if (a.selt) {
+    // fused launch: entry j of the row is 8 words (id | fmt << 16, weight
+    // bits, then the 32-bit halves of its gate, up and down offsets); lane L
+    // writes word L & 7 of entry L >> 3 into every copy
+    const int nw = a.k * kSelWords, ent = lane >> 3, fld = lane & 7;
+    const int id_e = __shfl(my_id, ent, 64);
+    const uint32_t w_e = __shfl(__builtin_bit_cast(uint32_t, w), ent, 64);
+    if (lane < nw) {
+      const uint32_t* f = reinterpret_cast<const uint32_t*>(refs + id_e);   // fmt, reserved, gate, up, down
+      const uint32_t v = fld == 0 ? (static_cast<uint32_t>(id_e) | (f[0] << 16)) : fld == 1 ? w_e : f[fld];
+      uint64_t* o = a.selt + static_cast<size_t>(r) * nw + lane;
+#pragma unroll
+      for (int c = 0; c < kSelRep; ++c) tstore(o + c * kSelRepWords, tag, v);
     }
   }
 }
@@ -1156,22 +1174,22 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   int* ids = reinterpret_cast<int*>(eref + kMaxRows * kMaxK);
   float* wv = reinterpret_cast<float*>(ids + kMaxRows * kMaxK);
   const int n = a.R * a.k;
-  // every worker waits here: one lane polls one word until the selection
-  // shows up, so a thousand workgroups do not hammer the same lines, then the
-  // whole selection is read (and the words still missing are polled)
-  if (tid() == 0) (void)await_word(a.selt + n * kSelWords - 1, tag, a.err);
-  __syncthreads();
-  {
-    constexpr int PER = kMaxRows * kMaxK * kSelWords / kThreads;
+  // every worker waits here.  One wave polls the whole selection, a few words
+  // a lane: a thousand workgroups polling with every lane would hammer the
+  // same lines, and a single-word poll followed by a full read would cost a
+  // second round trip once the selection is there
+  if (tid() < 64) {
+    constexpr int PER = kMaxRows * kMaxK * kSelWords / 64;
+    const int lane = tid();
     uint32_t v[PER];
     await_batch<PER>(
-        [selt = a.selt, lim = n * kSelWords](int j) -> const uint64_t* {
-          const int i = tid() + j * kThreads;
+        [selt = a.selt + (bid % kSelRep) * kSelRepWords, lim = n * kSelWords, lane](int j) -> const uint64_t* {
+          const int i = lane + j * 64;
           return i < lim ? selt + i : nullptr;
         },
         tag, a.err, v);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) ew[tid() + j * kThreads] = v[j];
+    for (int j = 0; j < PER; ++j) ew[lane + j * 64] = v[j];
   }
   __syncthreads();
   if (tid() < n) {
@@ -1241,7 +1259,7 @@ WsLayout ws_layout(const moe_dims& d, int rows) {
   l.h = o;        o = align_up(o + 4 * pairs * d.inter, 256);
   l.part = o;     o = align_up(o + 4 * pairs * d.hidden, 256);
   l.lgt = o;      o = align_up(o + 16 * static_cast<size_t>(rows) * d.n_experts, 256);
-  l.selt = o;     o = align_up(o + 8 * dev::kSelWords * static_cast<size_t>(rows) * d.top_k, 256);
+  l.selt = o;     o = align_up(o + 8 * static_cast<size_t>(dev::kSelRep) * dev::kSelRepWords, 256);
   l.ht = o;       o = align_up(o + 8 * pairs * d.inter, 256);
   l.part_t = o;   o = align_up(o + 8 * pairs * d.hidden, 256);
   l.total = o;
