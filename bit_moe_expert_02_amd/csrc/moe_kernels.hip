@@ -120,7 +120,6 @@ struct Args {
                                   // (moe_layer), so the gate/up launch skips it
   int shared_own_down;            // 1: the shared expert's down has its own workgroups
                                   // (fused launch), so the down list skips it
-  int base_sd;                    // fused launch: first shared-down workgroup
   int base_y;                     // fused launch: first combine workgroup
 };
 
@@ -197,13 +196,15 @@ struct Shape {
   static constexpr int LDS_STAGE = cmax(kNTB * I * 4, kNTB * H * 2);
   static constexpr int LDS_WITH_STAGE = LDS_BYTES + LDS_STAGE;
   // fused launch: the workers' selection words, expert refs, ids and weights
-  // sit at the start of the dynamic region until the slot table is built
+  // sit in the record area until the slot table is built (past the staging
+  // area when the record area is too small): the staging area keeps x
   static constexpr int LDS_SEL_WORDS = kMaxRows * kMaxK * kSelWords * 4;
   static constexpr int LDS_SEL = LDS_SEL_WORDS + kMaxRows * kMaxK * (static_cast<int>(sizeof(moe_expert_ref)) + 8);
+  static constexpr int LDS_SEL_OFF = LDS_REC >= LDS_SEL ? 0 : LDS_WITH_STAGE;
   // the selection workgroup keeps the whole expert table (up to 64 * kSelQ
   // entries) there
   static constexpr int LDS_REFS = 64 * kSelQ * static_cast<int>(sizeof(moe_expert_ref));
-  static constexpr int LDS_LAYER = cmax(cmax(LDS_WITH_STAGE, LDS_SEL), LDS_REFS);
+  static constexpr int LDS_LAYER = cmax(cmax(LDS_WITH_STAGE, LDS_SEL_OFF + LDS_SEL), LDS_REFS);
 };
 
 // tiles of a format tag (device side: the tag comes from the expert table)
@@ -384,6 +385,53 @@ __device__ __forceinline__ void build_tern_table(uint32_t* table) {
 // STAGE_LOCAL: records are built here from x (shared expert riding in the
 // router launch); otherwise they are copied from the per-layer record buffer.
 // ---------------------------------------------------------------------------
+// Fused launch: the staging area keeps x row g_xrow (bf16) between gate/up
+// items, with the largest |x| as fp32 bits in g_xmax, so that an item of that
+// row loads nothing but its weights.  The workers stage row 0 at their start,
+// before they wait for anything; -1: nothing staged.
+__shared__ int g_xrow;
+__shared__ uint32_t g_xmax;
+
+// Stages x row r into the staging area and records it as g_xrow / g_xmax.
+template <class S>
+__device__ __forceinline__ void stage_x_row(const Args& a, int r, uint8_t* lds) {
+  constexpr int H = S::kH, XCH = (H / 8 + kThreads - 1) / kThreads;
+  __shared__ uint32_t red[kThreads / 64];
+  const Buf xb = make_buf(reinterpret_cast<const uint8_t*>(a.x), static_cast<uint32_t>(a.R * H * 2));
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
+  u32x4 xq[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int ch = tid() + i * kThreads;
+    xq[i] = bload128(xb, ch < H / 8 ? static_cast<uint32_t>((r * H + 8 * ch) * 2) : 0x7FFFFFF0u);
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int ch = tid() + i * kThreads;
+    if (ch < H / 8) {
+      *reinterpret_cast<u32x4*>(xs + 8 * ch) = xq[i];
+      const uint32_t w[4] = {xq[i].x, xq[i].y, xq[i].z, xq[i].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = (w[q] & 0x7FFFu) << 16, hi = (w[q] >> 16 & 0x7FFFu) << 16;
+        m = m > lo ? m : lo;
+        m = m > hi ? m : hi;
+      }
+    }
+  }
+  m = wave_max_u32(m);
+  if ((tid() & 63) == 0) red[tid() >> 6] = m;
+  __syncthreads();
+  if (tid() == 0) {
+    uint32_t mm = 0;
+    for (int w = 0; w < kThreads / 64; ++w) mm = mm > red[w] ? mm : red[w];
+    g_xmax = mm;
+    g_xrow = r;
+  }
+  __syncthreads();
+}
+
 template <class S, class F, bool STAGE_LOCAL, bool TAG>
 __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, int tile, uint8_t* lds, uint32_t tag) {
   using C = TileCfg<F, S::kH, true>;
@@ -412,7 +460,8 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
     // trip to memory covers both
     constexpr int XCH = (H / 8 + kThreads - 1) / kThreads;   // 16-byte chunks per thread and row
     u32x4 xq[kNTB][XCH];
-    if constexpr (STAGE_LOCAL) {
+    const bool cached = TAG && kNTB == 1 && uniform(g_xrow) == uniform(sl.row[t0]);
+    if (STAGE_LOCAL && !cached) {
       // buffer loads: chunks past the row or rows past the batch read an
       // offset beyond the buffer and come back as zeros, without branches
       const Buf xb = make_buf(reinterpret_cast<const uint8_t*>(a.x), static_cast<uint32_t>(a.R * H * 2));
@@ -430,7 +479,15 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
     }
     st.load(0, mats, rows, I, valid);            // weights in flight while records are staged
     __syncthreads();
-    if constexpr (STAGE_LOCAL) {
+    if (STAGE_LOCAL && cached) {
+      if (tid() == 0) {
+        sig_exp[0] = sigma_exp<F>(g_xmax);
+        inv_sigma[0] = __builtin_ldexpf(1.0f, -sig_exp[0]);
+        srcs[0] = lds + S::LDS_BYTES;
+      }
+      __syncthreads();
+      build_records<F, H, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
+    } else if constexpr (STAGE_LOCAL) {
       uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
 #pragma unroll
       for (int t = 0; t < kNTB; ++t) {
@@ -460,6 +517,10 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         sig_exp[t] = sigma_exp<F>(m);
         inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
         srcs[t] = xs + t * H;
+        if (TAG && kNTB == 1) {
+          g_xrow = sl.row[t0];
+          g_xmax = m;
+        }
       }
       __syncthreads();
       build_records<F, H, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
@@ -625,7 +686,8 @@ __device__ __forceinline__ void run_slot(const Args& a, const SlotEntry& sl, int
 // weights come from LDS (ids[R*k], wv[R*k]).
 template <class S>
 __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, const float* wv, SlotTable* tab,
-                                 bool write_order, const moe_expert_ref* eref = nullptr) {
+                                 bool write_order, const moe_expert_ref* eref = nullptr,
+                                 const moe_expert_ref* shref = nullptr) {
   __shared__ int tg[kMaxSlots + 1], td[kMaxSlots + 1];
   const int lane = tid();
   const int n = a.R * a.k;
@@ -661,7 +723,7 @@ __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, 
   if (a.shared && lane < a.R) {
     SlotEntry& e = tab->e[n_active];
     if (lane == 0) {
-      const moe_expert_ref ref = *a.shared;
+      const moe_expert_ref ref = shref ? *shref : *a.shared;
       e.ref = ref;
       e.expert = -1;
       e.nt = a.R;
@@ -1005,10 +1067,30 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_prep(Args a) {
   prep_wg<S>(a, blockIdx.x - 1);
 }
 
-// Work items of one list, strided over `nw` workers (this is worker w): each
-// item finds its slot in the offsets (binary search over at most 65 slots),
-// copies the slot entry to LDS and runs the tile.  STAGE as in run_slot;
-// the list is the down list for STAGE 0, else the gate/up list.
+// One work item: the slot whose range [offs[slot], offs[slot + 1]) holds it
+// (offs in LDS; binary search over at most 65 slots), its entry copied to
+// LDS, then that slot's tile.  Ends with a barrier: LDS and the slot entry
+// are reused by the next item.
+template <class S, int STAGE, bool TAG>
+__device__ __forceinline__ void run_item(const Args& a, const SlotTable* tab, const int* offs, int ns, int item,
+                                         SlotEntry& sl, uint8_t* lds, uint32_t tag) {
+  int lo = 0, hi = ns - 1;             // largest slot with offs[slot] <= item
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= item) lo = mid;
+    else hi = mid - 1;
+  }
+  const int slot = lo, tile = item - offs[lo];
+  if (tid() < static_cast<int>(sizeof(SlotEntry) / 4))
+    reinterpret_cast<uint32_t*>(&sl)[tid()] = reinterpret_cast<const uint32_t*>(&tab->e[slot])[tid()];
+  __syncthreads();
+  run_slot<S, STAGE, TAG>(a, sl, tile, lds, tag);
+  __syncthreads();
+}
+
+// Work items of one list, strided over `nw` workers (this is worker w).
+// STAGE as in run_slot; the list is the down list for STAGE 0, else the
+// gate/up list.
 template <class S, int STAGE, bool TAG>
 __device__ __forceinline__ void run_items(const Args& a, const SlotTable* tab, int w, int nw, uint8_t* lds,
                           uint32_t tag = 0) {
@@ -1020,21 +1102,7 @@ __device__ __forceinline__ void run_items(const Args& a, const SlotTable* tab, i
   if (w >= n_items) return;
   for (int i = tid(); i <= ns; i += kThreads) offs[i] = off_g[i];
   __syncthreads();
-  for (int item = w; item < n_items; item += nw) {
-    int lo = 0, hi = ns - 1;           // largest slot with offs[slot] <= item
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (offs[mid] <= item) lo = mid;
-      else hi = mid - 1;
-    }
-    const int slot = lo, tile = item - offs[lo];
-    if (tid() < static_cast<int>(sizeof(SlotEntry) / 4))
-      reinterpret_cast<uint32_t*>(&sl)[tid()] =
-          reinterpret_cast<const uint32_t*>(&tab->e[slot])[tid()];
-    __syncthreads();
-    run_slot<S, STAGE, TAG>(a, sl, tile, lds, tag);
-    __syncthreads();                    // the slot entry and LDS are reused
-  }
+  for (int item = w; item < n_items; item += nw) run_item<S, STAGE, TAG>(a, tab, offs, ns, item, sl, lds, tag);
 }
 
 // gateup: h = silu(W_gate x) * (W_up x) for every (slot, tile) item.
@@ -1103,10 +1171,10 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
 // ---------------------------------------------------------------------------
 // [0, E)              router GEMV, logits published as tagged words
 // [E, E + R)          selection of row blockIdx - E (one wave), published tagged
-// [E + R, base_sd)    the shared expert's gate/up tiles (need only x)
-// [base_sd, base_b)   the shared expert's down tiles (need only the shared h)
-// [base_b, base_c)    gate/up workers over the routed (slot, tile) items
-// [base_c, base_y)    down workers over the routed items
+// [base_b, base_y)    workers over one list of items: the shared expert's
+//                     gate/up tiles (they need only x and stream while the
+//                     selection is made), the routed gate/up (slot, tile)
+//                     items, then the down items, routed and shared
 // [base_y, ...)       combine: one output element per thread
 // Every role waits only on roles with lower workgroup ids, which the
 // dispatcher has started before it, so the waits always end; the workers
@@ -1137,47 +1205,61 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     if (tid() < 64) select_row_tagged(a, bid - a.E, sel, wsel, tag, refs);
     return;
   }
-  if (bid < a.base_b) {
-    // shared expert: gate/up tiles [E + R, base_sd), then its down tiles
-    // [base_sd, base_b), which wait for the shared h only and stream while the
-    // selection is still being made
-    __shared__ SlotEntry se;
-    if (tid() == 0) {
-      se.ref = *a.shared;
-      se.expert = -1;
-      se.nt = a.R;
-      for (int r = 0; r < a.R; ++r) {
-        se.row[r] = r;
-        se.pair[r] = a.R * a.k + r;
-        se.w[r] = 1.0f;
-      }
-    }
-    __syncthreads();
-    if (bid < a.base_sd) {
-      const int tile = bid - a.E - a.R;
-      if (tile < tiles_of<S, true>(se.ref.fmt)) run_slot<S, 2, true>(a, se, tile, lds, tag);
-    } else {
-      const int tile = bid - a.base_sd;
-      if (tile < tiles_of<S, false>(se.ref.fmt)) run_slot<S, 0, true>(a, se, tile, lds, tag);
-    }
-    return;
-  }
   if (bid >= a.base_y) {
     combine_out<S>(a, (bid - a.base_y) * kThreads + tid(), tag);
     return;
   }
-  // workers: the selection of every row, then the slot table in LDS; the
-  // selection's staging shares the dynamic region with the tiles' records
+  // workers.  Worker w takes items w, w + nw, ... of one list: the shared
+  // expert's gate/up tiles, then the routed gate/up items, then the down
+  // items (routed and shared).  A down item waits only for gate/up items,
+  // which come earlier in the list, so the worker holding them has done them
+  // or runs them (every worker is started: the roles before the workers never
+  // wait on them); its weights are in flight while it waits for h.
+  // The shared expert's table entry is read once, at the start, and kept in
+  // LDS: nothing after the selection waits on a global load that could sit
+  // behind the weight traffic.
+  const int w = bid - a.base_b, nw = a.nb;
   __shared__ SlotTable tab;
-  uint32_t* ew = reinterpret_cast<uint32_t*>(lds);
-  moe_expert_ref* eref = reinterpret_cast<moe_expert_ref*>(lds + S::LDS_SEL_WORDS);
+  __shared__ moe_expert_ref shref;
+  __shared__ SlotEntry sl;
+  __shared__ int offs[2][kMaxSlots + 2];
+  if (tid() == 0 && a.shared) shref = *a.shared;
+  stage_x_row<S>(a, 0, lds);   // before any wait: every gate/up item of row 0 finds x here
+
+  const int nsh = a.shared ? uniform(tiles_of<S, true>(shref.fmt)) : 0;
+  int i = w;
+  if (i < nsh) {
+    // shared gate/up tiles need only x: they stream while the selection is
+    // made.  They wait until router workgroup w % E has its logit out, so the
+    // router's own loads do not queue behind this traffic.
+    if (tid() == 0) {
+      sl.ref = shref;
+      sl.expert = -1;
+      sl.nt = a.R;
+      for (int r = 0; r < a.R; ++r) {
+        sl.row[r] = r;
+        sl.pair[r] = a.R * a.k + r;
+        sl.w[r] = 1.0f;
+      }
+      (void)await_word(a.lgt + 2 * (w % a.E), tag, a.err);
+    }
+    __syncthreads();
+    for (; i < nsh; i += nw) {
+      run_slot<S, 2, true>(a, sl, i, lds, tag);
+      __syncthreads();   // LDS is reused next
+    }
+  }
+  // the selection of every row, then the slot table in LDS; the selection's
+  // staging shares the dynamic region with the tiles' records
+  uint32_t* ew = reinterpret_cast<uint32_t*>(lds + S::LDS_SEL_OFF);
+  moe_expert_ref* eref = reinterpret_cast<moe_expert_ref*>(lds + S::LDS_SEL_OFF + S::LDS_SEL_WORDS);
   int* ids = reinterpret_cast<int*>(eref + kMaxRows * kMaxK);
   float* wv = reinterpret_cast<float*>(ids + kMaxRows * kMaxK);
   const int n = a.R * a.k;
-  // every worker waits here.  One wave polls the whole selection, a few words
-  // a lane: a thousand workgroups polling with every lane would hammer the
-  // same lines, and a single-word poll followed by a full read would cost a
-  // second round trip once the selection is there
+  // One wave polls the whole selection, a few words a lane: a thousand
+  // workgroups polling with every lane would hammer the same lines, and a
+  // single-word poll followed by a full read would cost a second round trip
+  // once the selection is there
   if (tid() < 64) {
     constexpr int PER = kMaxRows * kMaxK * kSelWords / 64;
     const int lane = tid();
@@ -1193,21 +1275,31 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   }
   __syncthreads();
   if (tid() < n) {
-    const uint32_t* w = ew + tid() * kSelWords;
-    ids[tid()] = static_cast<int>(w[0] & 0xFFFFu);
-    wv[tid()] = __builtin_bit_cast(float, w[1]);
+    const uint32_t* e = ew + tid() * kSelWords;
+    ids[tid()] = static_cast<int>(e[0] & 0xFFFFu);
+    wv[tid()] = __builtin_bit_cast(float, e[1]);
     moe_expert_ref& f = eref[tid()];
-    f.fmt = w[0] >> 16;
+    f.fmt = e[0] >> 16;
     f.reserved = 0;
-    f.gate = (static_cast<uint64_t>(w[3]) << 32) | w[2];
-    f.up = (static_cast<uint64_t>(w[5]) << 32) | w[4];
-    f.down = (static_cast<uint64_t>(w[7]) << 32) | w[6];
+    f.gate = (static_cast<uint64_t>(e[3]) << 32) | e[2];
+    f.up = (static_cast<uint64_t>(e[5]) << 32) | e[4];
+    f.down = (static_cast<uint64_t>(e[7]) << 32) | e[6];
   }
   __syncthreads();
-  if (tid() < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref);
+  if (tid() < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref, &shref);
   __syncthreads();
-  if (bid < a.base_c) run_items<S, 2, true>(a, &tab, bid - a.base_b, a.nb, lds, tag);
-  else run_items<S, 0, true>(a, &tab, bid - a.base_c, a.nc, lds, tag);
+  const int ns = uniform(tab.n_slots);
+  for (int q = tid(); q <= ns; q += kThreads) {
+    offs[0][q] = tab.gu_off[q];
+    offs[1][q] = tab.dn_off[q];
+  }
+  __syncthreads();
+  const int n_gu = uniform(tab.n_gu), n_dn = uniform(tab.n_dn);
+  for (; i < nsh + n_gu + n_dn; i += nw) {
+    const int j = i - nsh;
+    if (j < n_gu) run_item<S, 2, true>(a, &tab, offs[0], ns, j, sl, lds, tag);
+    else run_item<S, 0, true>(a, &tab, offs[1], ns, j - n_gu, sl, lds, tag);
+  }
 }
 
 // Combine: y[r] = sum over the row's experts in ascending id, then the shared
@@ -1289,10 +1381,16 @@ int check_dims(const moe_dims* d, int rows) {
 // one residency round: MOE_WAVES_PER_EU workgroups of 4 waves per CU, 256 CUs
 constexpr int kMaxGrid = MOE_WAVES_PER_EU * 256;
 int item_grid(int upper, int cap = kMaxGrid) { return upper < cap ? upper : cap; }
-// Fused launch: gate/up and down workers (the down workers come after every
-// gate/up worker, so they take the slots the gate/up workers leave free).
-constexpr int kFusedGU = kMaxGrid;
-constexpr int kFusedDN = kMaxGrid;
+// Fused launch: at most one residency round of workers, so that all of them
+// can be resident at once once the router and selection workgroups are done
+// (a down item may wait on a gate/up item of any worker).
+int fused_workers() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return MOE_WAVES_PER_EU * cus;
+}
 
 // Tags of fused calls: unique in the process, so no word a workspace holds
 // from an earlier call can carry the tag of a later one.
@@ -1315,14 +1413,13 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   a.lgt = reinterpret_cast<uint64_t*>(w8 + l.lgt);
   a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
   a.ht = reinterpret_cast<uint64_t*>(w8 + l.ht);
-  a.shared_early = 1;                       // the shared expert has its own workgroups
-  a.shared_own_down = 1;
-  a.base_sd = d->n_experts + rows + (sh ? S::MAX_TILES_GU : 0);
-  a.base_b = a.base_sd + (sh ? S::MAX_TILES_DN : 0);
-  a.nb = item_grid(n_routed * S::MAX_TILES_GU, kFusedGU);
-  a.base_c = a.base_b + a.nb;
-  a.nc = item_grid(n_routed * S::MAX_TILES_DN, kFusedDN);
-  a.base_y = a.base_c + a.nc;
+  a.shared_early = 1;     // the shared gate/up tiles are taken by the workers before the selection
+  a.shared_own_down = 0;  // the shared down tiles are items of the down workers
+  a.base_b = d->n_experts + rows;
+  a.nb = item_grid((sh ? S::MAX_TILES_GU : 0) + n_routed * S::MAX_TILES_GU + (n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN,
+                   fused_workers());
+  a.base_c = a.base_y = a.base_b + a.nb;
+  a.nc = 0;
   const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;
   const size_t lds = S::LDS_LAYER;
   int ev = 0;
