@@ -223,15 +223,37 @@ __device__ __forceinline__ int tiles_of(uint32_t fmt) {
 // ---------------------------------------------------------------------------
 // activation records
 // ---------------------------------------------------------------------------
+// A bf16 source row in LDS is read through an LDS pointer: a generic (flat)
+// access also counts as a memory load, and waiting for it would wait for
+// every weight load in flight as well.  (fp32 rows are still read through
+// generic pointers.)
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <bool LDS>
+__device__ __forceinline__ v2u ld8(const void* src, int i) {
+  if constexpr (LDS)
+    return reinterpret_cast<const __attribute__((address_space(3))) v2u*>(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(src)))[i];
+  else return static_cast<const v2u*>(src)[i];
+}
+template <bool LDS>
+__device__ __forceinline__ v4u ld16(const void* src, int i) {
+  if constexpr (LDS)
+    return reinterpret_cast<const __attribute__((address_space(3))) v4u*>(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(src)))[i];
+  else return static_cast<const v4u*>(src)[i];
+}
+
 // SUBV values starting at element e0 (a multiple of 4), zero at and beyond KR
-template <int SUBV, int KR, bool BF16>
+template <int SUBV, int KR, bool BF16, bool LDS = false>
 __device__ __forceinline__ void load_vals(const void* src, int e0, float (&v)[SUBV]) {
 #pragma unroll
   for (int c = 0; c < SUBV / 4; ++c) {
     const int e = e0 + 4 * c;
     if (e < KR) {
       if constexpr (BF16) {
-        const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + e);
+        const v2u q = ld8<LDS>(src, e / 4);
         v[4 * c + 0] = bf16_bits_to_f32(q.x & 0xFFFFu);
         v[4 * c + 1] = bf16_bits_to_f32(q.x >> 16);
         v[4 * c + 2] = bf16_bits_to_f32(q.y & 0xFFFFu);
@@ -260,22 +282,20 @@ __device__ __forceinline__ int sigma_exp(uint32_t max_bits) {
 
 // Largest |value| of a row, as monotone fp32 bits; called by every thread of
 // the workgroup, result valid in all threads.
-template <int KR, bool BF16>
+template <int KR, bool BF16, bool LDS = false>
 __device__ __forceinline__ uint32_t row_max_bits(const void* src, uint32_t* red) {
   constexpr int PER = BF16 ? 8 : 4;
   constexpr int CH = (KR / PER + kThreads - 1) / kThreads;
-  uint4 qs[CH];
+  v4u qs[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int c = tid() + i * kThreads;
-    qs[i] = c < KR / PER ? *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) +
-                                                           static_cast<size_t>(c) * 16)
-                         : uint4{0, 0, 0, 0};
+    qs[i] = c < KR / PER ? ld16<LDS>(src, c) : v4u{0, 0, 0, 0};
   }
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const uint4 q = qs[i];
+    const v4u q = qs[i];
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -299,7 +319,7 @@ __device__ __forceinline__ uint32_t row_max_bits(const void* src, uint32_t* red)
 }
 
 // Records of `nb` rows into LDS, with sigma given per row (sig_exp[t]).
-template <class F, int KR, bool BF16>
+template <class F, int KR, bool BF16, bool LDS = false>
 __device__ __forceinline__ void build_records(const void* const* rows, int nb, const int* sig_exp,
                                               uint8_t* rec, int item0, int stride) {
   constexpr int NBU = F::units(KR);
@@ -309,7 +329,7 @@ __device__ __forceinline__ void build_records(const void* const* rows, int nb, c
     const int t = item / PER_ROW, rem = item - t * PER_ROW;
     const int u = rem / F::SUBS, sub = rem - u * F::SUBS;
     float v[F::SUBV];
-    load_vals<F::SUBV, KR, BF16>(rows[t], u * F::UNIT + sub * F::SUBV, v);
+    load_vals<F::SUBV, KR, BF16, LDS>(rows[t], u * F::UNIT + sub * F::SUBV, v);
     const float sg = __builtin_ldexpf(1.0f, sig_exp[t]);
 #pragma unroll
     for (int i = 0; i < F::SUBV; ++i) v[i] *= sg;
@@ -486,7 +506,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         srcs[0] = lds + S::LDS_BYTES;
       }
       __syncthreads();
-      build_records<F, H, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
+      build_records<F, H, true, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
     } else if constexpr (STAGE_LOCAL) {
       uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
 #pragma unroll
@@ -523,7 +543,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         }
       }
       __syncthreads();
-      build_records<F, H, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
+      build_records<F, H, true, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
     } else {
       // copy this format's records of the rows from the per-layer buffer
       // straight into LDS (global_load_lds_dwordx4): each wave moves 1 KB per
@@ -624,14 +644,14 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
     }
     __syncthreads();
     for (int t = 0; t < nb; ++t) {
-      const uint32_t m = row_max_bits<I, false>(srcs[t], red);
+      const uint32_t m = row_max_bits<I, false, TAG>(srcs[t], red);
       if (tid() == 0) {
         sig_exp[t] = sigma_exp<F>(m);
         inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
       }
     }
     __syncthreads();
-    build_records<F, I, false>(srcs, nb, sig_exp, rec, tid(), kThreads);
+    build_records<F, I, false, TAG>(srcs, nb, sig_exp, rec, tid(), kThreads);
     __syncthreads();
     float acc[NPG][kNTB] = {};
     st.template run<kNTB>(mats, rows, H, valid, rec, nb, acc, table);
