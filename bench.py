@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--pool", type=int, default=16)
     p.add_argument("--sweep", default="1,5,8", help="extra row counts reported beside the headline")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1)
+    p.add_argument("--cpu-rows", type=int, default=4)
     p.add_argument("--workload", default="decode_q2",
                    choices=["decode_q2", "stack40_mixed", "fp4_stack20", "fp4_prefill"],
                    help="decode_q2: the single-layer headline; the stacks time whole "
