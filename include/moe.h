@@ -197,8 +197,9 @@ int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, vo
  * Deterministic: the same inputs give bitwise the same y.
  * rows <= MOE_MAX_DECODE_ROWS: the decode path, any formats.
  * MOE_MAX_DECODE_ROWS < rows <= MOE_MAX_PREFILL_ROWS: the prefill path on the
- * scaled matrix cores.  x and h = silu(W_gate x) * (W_up x) are quantised to
- * MXFP8 (as moe_quant_mxfp8) before their products; every selected expert
+ * scaled matrix cores.  x is quantised to MXFP8 (as moe_quant_mxfp8) for the
+ * gate/up products; h = silu(W_gate x) * (W_up x) is rounded to f16 for the
+ * down products (f16 x MXFP4 on the matrix cores); every selected expert
  * must be MXFP4 (a row that selects another format comes out NaN); shared
  * must be NULL (else MOE_ESHAPE).  The workspace is moe_workspace_bytes(dims,
  * rows) (about rows * top_k * (hidden * 4 + inter) bytes). */
@@ -207,14 +208,19 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
                    void* stream);
 
-/* The whole layer, same results as moe_route followed by moe_expert_ffn, in
- * one launch whose workgroups hand logits, selections, h and partial outputs
- * to each other through words tagged with the call's tag (router, selection,
- * shared-expert gate/up and down, routed gate/up, routed down, fixed-order
- * combine).  The shared expert and the down weights stream while their
- * inputs are still being computed.  idx and wts are outputs as in moe_route.
- * Should a hand-off ever fail to arrive, its waits end after a bounded spin
- * and y comes out NaN. */
+/* The whole layer, same results as moe_route followed by moe_expert_ffn
+ * (rows <= MOE_MAX_DECODE_ROWS), in one launch whose workgroups hand logits,
+ * selections, h and partial outputs to each other through words tagged with
+ * the call's tag: router, selection, then workers over one list of items
+ * (the shared expert's gate/up tiles, the routed gate/up items, then the
+ * down items), then a fixed-order combine.  The shared expert streams while
+ * the selection is made and down weights stream while h is still being
+ * computed.  idx and wts are outputs as in moe_route.
+ * The launch holds at most one residency round of workers (sized from the
+ * device's compute-unit count), since a down item may wait on a gate/up item
+ * of any worker: a kernel on another stream that keeps compute units busy
+ * meanwhile can only delay it.  Should a hand-off ever fail to arrive, its
+ * waits end after a bounded spin and y comes out NaN. */
 int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, const void* weights, const moe_expert_ref* experts,
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
