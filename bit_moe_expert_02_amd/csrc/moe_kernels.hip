@@ -59,7 +59,10 @@ constexpr int kSelWords = 8;
 // so a thousand polling workgroups spread over many memory channels instead
 // of queueing on the same few lines.  Copy 0 is the one the combine reads.
 constexpr int kSelRep = 16;
-constexpr int kSelRepWords = kMaxRows * kMaxK * kSelWords;
+constexpr int kSelEntryWords = kMaxRows * kMaxK * kSelWords;
+// word kSelEntryWords of each copy: "the logits are all out" (payload 1),
+// published by the selection of row 0 as soon as its wait ends
+constexpr int kSelRepWords = kSelEntryWords + 64;
 
 // One entry of the slot table: a distinct selected expert (or the shared one)
 // and the rows it serves.
@@ -925,6 +928,7 @@ __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel
         return e < E ? lg + 2 * e + (j & 1) : nullptr;
       },
       tag, a.err, half);
+  if (r == 0 && a.selt && lane < kSelRep) tstore(a.selt + lane * kSelRepWords + kSelEntryWords, tag, 1u);
   double lv[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q)
@@ -1250,8 +1254,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   int i = w;
   if (i < nsh) {
     // shared gate/up tiles need only x: they stream while the selection is
-    // made.  They wait until router workgroup w % E has its logit out, so the
-    // router's own loads do not queue behind this traffic.
+    // made.  They wait until the selection has every logit, so neither the
+    // router's loads nor the selection's poll queue behind this traffic.
     if (tid() == 0) {
       sl.ref = shref;
       sl.expert = -1;
@@ -1261,7 +1265,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
         sl.pair[r] = a.R * a.k + r;
         sl.w[r] = 1.0f;
       }
-      (void)await_word(a.lgt + 2 * (w % a.E), tag, a.err);
+      (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err);
     }
     __syncthreads();
     for (; i < nsh; i += nw) {
@@ -1281,7 +1285,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   // single-word poll followed by a full read would cost a second round trip
   // once the selection is there
   if (tid() < 64) {
-    constexpr int PER = kMaxRows * kMaxK * kSelWords / 64;
+    constexpr int PER = kSelEntryWords / 64;
     const int lane = tid();
     uint32_t v[PER];
     await_batch<PER>(
