@@ -500,7 +500,9 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
         }
       }
     }
-    st.load(0, mats, rows, I, valid);            // weights in flight while records are staged
+    // weights in flight while records are staged; with one load phase they
+    // stay in registers, so the next rows of the slot reuse them
+    if (Stream<F, H, LPR, 2, C::G>::P > 1 || t0 == 0) st.load(0, mats, rows, I, valid);
     __syncthreads();
     if (STAGE_LOCAL && cached) {
       if (tid() == 0) {
@@ -616,7 +618,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
   const int nt_all = uniform(sl.nt);
   for (int t0 = 0; t0 < nt_all; t0 += kNTB) {
     const int nb = nt_all - t0 < kNTB ? nt_all - t0 : kNTB;
-    st.load(0, mats, rows, H, valid);
+    if (Stream<F, I, LPR, NPG, C::G>::P > 1 || t0 == 0) st.load(0, mats, rows, H, valid);   // kept for later rows
     __syncthreads();
     if constexpr (TAG) {
       // h comes from gate/up workgroups of the same launch: wait for its
