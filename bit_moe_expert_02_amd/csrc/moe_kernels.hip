@@ -116,6 +116,7 @@ struct Args {
   uint64_t* selt;                 // kSelRep copies of [R x k x kSelWords] selection entries
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
   int base_b, nb, base_c, nc;     // gate/up and down worker ranges of the fused launch
+  int nsw;                        // fused launch: workers that take the shared gate/up tiles
   // stack decode: the fused combine also writes the next layer's input
   const float* noise;             // [R x H] fp32 added to y before rounding, or null
   uint16_t* x_next;               // [R x H] bf16 out, or null
@@ -1253,8 +1254,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   stage_x_row<S>(a, 0, lds);   // before any wait: every gate/up item of row 0 finds x here
 
   const int nsh = a.shared ? uniform(tiles_of<S, true>(shref.fmt)) : 0;
-  int i = w;
-  if (i < nsh) {
+  if (w < a.nsw && w < nsh) {
     // shared gate/up tiles need only x: they stream while the selection is
     // made.  They wait until the selection has every logit, so neither the
     // router's loads nor the selection's poll queue behind this traffic.
@@ -1270,8 +1270,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
       (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err);
     }
     __syncthreads();
-    for (; i < nsh; i += nw) {
-      run_slot<S, 2, true>(a, sl, i, lds, tag);
+    for (int t = w; t < nsh; t += a.nsw) {
+      run_slot<S, 2, true>(a, sl, t, lds, tag);
       __syncthreads();   // LDS is reused next
     }
   }
@@ -1321,8 +1321,10 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   }
   __syncthreads();
   const int n_gu = uniform(tab.n_gu), n_dn = uniform(tab.n_dn);
-  for (; i < nsh + n_gu + n_dn; i += nw) {
-    const int j = i - nsh;
+  // the routed list starts at worker nsw: the workers holding shared tiles
+  // get its later positions, so the routed gate/up items start on free
+  // workers as soon as the selection is out
+  for (int j = (w - a.nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
     if (j < n_gu) run_item<S, 2, true>(a, &tab, offs[0], ns, j, sl, lds, tag);
     else run_item<S, 0, true>(a, &tab, offs[1], ns, j - n_gu, sl, lds, tag);
   }
@@ -1410,6 +1412,10 @@ int item_grid(int upper, int cap = kMaxGrid) { return upper < cap ? upper : cap;
 // Fused launch: at most one residency round of workers, so that all of them
 // can be resident at once once the router and selection workgroups are done
 // (a down item may wait on a gate/up item of any worker).
+// workers that take the shared expert's gate/up tiles (before the selection,
+// several each); the others are free for routed gate/up items at once
+constexpr int kSharedWorkers = 576;
+
 int fused_workers() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -1446,6 +1452,7 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
                    fused_workers());
   a.base_c = a.base_y = a.base_b + a.nb;
   a.nc = 0;
+  a.nsw = item_grid(kSharedWorkers, a.nb);
   const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;
   const size_t lds = S::LDS_LAYER;
   int ev = 0;
