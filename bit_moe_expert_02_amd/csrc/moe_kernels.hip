@@ -1,22 +1,23 @@
 // gfx950 kernels of the routed-MoE expert FFN and the C-ABI entry points
 // that launch them.
 //
-// One layer call runs five kernels on the caller's stream.  No kernel waits
-// on another workgroup of its own launch: on MI355X a device-scope release
-// (or a contended atomic) from hundreds of workgroups serialises across the
-// eight XCDs, so every cross-workgroup hand-off is a kernel boundary.
-//   route    router GEMV (fp64 sums), one workgroup per expert; beside it,
-//            workgroups that build the activation records of every weight
-//            format, and the shared expert's gate/up tiles (its weights
-//            stream while the router runs)
-//   select   one workgroup: top-k per row by logit + bias, ties to the lower
-//            id; softmax of the unbiased logits over the selection; the slot
-//            table of distinct experts and the rows each serves
-//   gateup   one workgroup per (distinct expert, tile of channels):
-//            h = silu(W_gate x) * (W_up x) in fp32
-//   down     one workgroup per (expert, tile of outputs): w * (W_down h)
-//   combine  y = the row's expert outputs in ascending id, then the shared
-//            expert -- a fixed order, so y is bitwise reproducible
+// moe_layer is one launch (k_layer) whose workgroups hand work to each other
+// through tagged words in the workspace (a 64-bit word: call tag << 32 |
+// payload, written and polled with relaxed device-scope accesses; a word
+// counts only once it carries this call's tag, so no fences and no counters):
+//   router     one workgroup per expert: logits with fp64 sums
+//   selection  one wave per row: top-k by logit + bias, ties to the lower id,
+//              softmax of the unbiased logits over the selection; published
+//              with each expert's matrix offsets in 16 copies
+//   workers    one residency round of workgroups over one list of items: the
+//              shared expert's gate/up tiles (before the selection), the
+//              routed gate/up items h = silu(W_gate x) * (W_up x), then the
+//              down items w * (W_down h) (routed and shared)
+//   combine    y = the row's expert outputs in ascending id, then the shared
+//              expert -- a fixed order, so y is bitwise reproducible
+// moe_route and moe_expert_ffn run the same tiles as separate kernels (route,
+// select, prep, gate/up, down, combine) with kernel boundaries as the only
+// synchronisation.
 //
 // The method: "DeepSeek-V4.1-Flash served three ways on 4xL20"
 // (lcz.me/topic/2356) section 1 (layer shape, top-6 of 384 plus one shared
@@ -115,15 +116,13 @@ struct Args {
   uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
   uint64_t* selt;                 // kSelRep copies of [R x k x kSelWords] selection entries
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
-  int base_b, nb, base_c, nc;     // gate/up and down worker ranges of the fused launch
+  int base_b, nb;                 // fused launch: first worker workgroup, number of workers
   int nsw;                        // fused launch: workers that take the shared gate/up tiles
   // stack decode: the fused combine also writes the next layer's input
   const float* noise;             // [R x H] fp32 added to y before rounding, or null
   uint16_t* x_next;               // [R x H] bf16 out, or null
   int shared_early;               // 1: the shared expert's gate/up runs beside the router
                                   // (moe_layer), so the gate/up launch skips it
-  int shared_own_down;            // 1: the shared expert's down has its own workgroups
-                                  // (fused launch), so the down list skips it
   int base_y;                     // fused launch: first combine workgroup
 };
 
@@ -754,7 +753,7 @@ __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, 
       e.expert = -1;
       e.nt = a.R;
       tg[n_active] = a.shared_early ? 0 : tiles_of<S, true>(ref.fmt);
-      td[n_active] = a.shared_own_down ? 0 : tiles_of<S, false>(ref.fmt);
+      td[n_active] = tiles_of<S, false>(ref.fmt);
     }
     e.row[lane] = lane;
     e.pair[lane] = n + lane;
@@ -886,8 +885,10 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
 }
 
 // Top-k of one row by key = logit + bias, ties to the lower id; weights are
-// the softmax of the unbiased logits over the selection.  One wave per row;
-// the logits come from the previous kernel, so plain loads see them.
+// the softmax of the unbiased logits over the selection.  One wave per row,
+// given the lane's logits (lv) and biases of experts lane + 64 q.  Each of
+// the k rounds takes the wave's largest key (f64 max over DPP), then the
+// lowest id holding it (ballots), and retires that entry.
 __device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ],
                                            const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
                                            const moe_expert_ref* refs);
@@ -1446,12 +1447,10 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
   a.ht = reinterpret_cast<uint64_t*>(w8 + l.ht);
   a.shared_early = 1;     // the shared gate/up tiles are taken by the workers before the selection
-  a.shared_own_down = 0;  // the shared down tiles are items of the down workers
   a.base_b = d->n_experts + rows;
   a.nb = item_grid((sh ? S::MAX_TILES_GU : 0) + n_routed * S::MAX_TILES_GU + (n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN,
                    fused_workers());
-  a.base_c = a.base_y = a.base_b + a.nb;
-  a.nc = 0;
+  a.base_y = a.base_b + a.nb;
   a.nsw = item_grid(kSharedWorkers, a.nb);
   const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;
   const size_t lds = S::LDS_LAYER;
