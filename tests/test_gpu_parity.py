@@ -114,6 +114,23 @@ def test_tiny_topk_max():
     del base
 
 
+def test_tiny_selection_limits():
+    """The selection and its hand-off at their limits: 500 experts (a ragged
+    last lane group of the 8 per lane), top_k = 8, 8 rows (64 entries, every
+    word of a published copy), mixed formats, a Q8 shared expert and a bias."""
+    wl = synth.Workload("tiny_limits", 12, 512, 256, 500, 8, "MIX", "Q8", use_bias=True, rows=(8,))
+    xbits = synth.x_bf16(wl, 0, 8, 0)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    need = sorted(set(idx.reshape(-1).tolist()))
+    _say("tiny limits: experts", len(need))
+    dl = LY.DeviceLayer(wl, 0, materialize=need)
+    gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), 8)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    err = G.rel_l2_rows(gy, G.oracle_y(wl, 0, x, idx, w, list(range(8))))
+    _say("  rel L2 per row", err)
+    assert np.all(err <= G.REL_L2_TOL)
+
+
 # ------------------------------------------------------------------ real shapes
 def _real_case(wl, rows, stream, check_rows):
     xbits = synth.x_bf16(wl, 0, rows, stream)
