@@ -341,35 +341,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
   for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[rt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-  WFrag bf[4];
+  // Weight codes one K-step ahead; their e8m0 scales four K-steps at a time:
+  // the 16 scale bytes of a row for steps 4q .. 4q+3 are one aligned 16-byte
+  // load shared by the row's four lane groups (lane group g uses byte g of
+  // dword s % 4), instead of a one-byte load per fragment and step.
+  static_assert(S % 4 == 0, "scales are loaded four K-steps at a time");
+  const uint32_t nbk = static_cast<uint32_t>(H / 32), splane = static_cast<uint32_t>(I) * nbk * 16u;
+  auto scale_group = [&](int f, int q) {
+    return bload128(f < 2 ? mg : mu, splane + static_cast<uint32_t>(brow[f]) * nbk + 16u * q);
+  };
+  u32x4 bq[4], sg[4], sgn[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bf[f] = load_wfrag(f < 2 ? mg : mu, I, H, brow[f], 0, g);
+  for (int f = 0; f < 4; ++f) {
+    bq[f] = bload128(f < 2 ? mg : mu, (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(g)) * 16u);
+    sg[f] = scale_group(f, 0);
+  }
   ATile t;
   a_load(t, xb, xsb, src, H, 0);
   a_store(t, at[0], asc[0]);
   __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    WFrag bn[4];
-    if (s + 1 < S) {
-      a_load(t, xb, xsb, src, H, s + 1);
+  for (int s4 = 0; s4 < S; s4 += 4) {
+    if (s4 + 4 < S) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = load_wfrag(f < 2 ? mg : mu, I, H, brow[f], s + 1, g);
+      for (int f = 0; f < 4; ++f) sgn[f] = scale_group(f, s4 / 4 + 1);
     }
 #pragma unroll
-    for (int rt = 0; rt < kRowTiles; ++rt) {
-      if (rt < mt) {
-        uint32_t sa;
-        const v8i af = a_frag(at[s & 1], asc[s & 1], rt, j, g, sa);
+    for (int d = 0; d < 4; ++d) {
+      const int s = s4 + d;
+      u32x4 bn[4];
+      if (s + 1 < S) {
+        a_load(t, xb, xsb, src, H, s + 1);
 #pragma unroll
-        for (int f = 0; f < 4; ++f) acc[rt][f] = mfma_mx(af, bf[f].q, acc[rt][f], sa, bf[f].s);
+        for (int f = 0; f < 4; ++f)
+          bn[f] = bload128(f < 2 ? mg : mu,
+                           (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(4 * (s + 1) + g)) * 16u);
       }
-    }
-    if (s + 1 < S) {
-      a_store(t, at[(s + 1) & 1], asc[(s + 1) & 1]);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bf[f] = bn[f];
+      for (int rt = 0; rt < kRowTiles; ++rt) {
+        if (rt < mt) {
+          uint32_t sa;
+          const v8i af = a_frag(at[s & 1], asc[s & 1], rt, j, g, sa);
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const uint32_t sw = d == 0 ? sg[f].x : d == 1 ? sg[f].y : d == 2 ? sg[f].z : sg[f].w;
+            acc[rt][f] = mfma_mx(af, bq[f], acc[rt][f], sa, (sw >> (8 * g)) & 0xFFu);
+          }
+        }
+      }
+      if (s + 1 < S) {
+        a_store(t, at[(s + 1) & 1], asc[(s + 1) & 1]);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) bq[f] = bn[f];
+      }
+      __syncthreads();
     }
-    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sg[f] = sgn[f];
   }
   // epilogue: SwiGLU, h stored as f16 (round to nearest even)
 #pragma unroll
