@@ -43,6 +43,8 @@ using dev::bload128;
 using dev::bload8;
 using dev::make_buf;
 using dev::u32x4;
+using dev::u32x2;
+using dev::bload64;
 using dev::uniform;
 
 constexpr int kThreads = 256;
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
   auto scale_group = [&](int f, int q) {
     return bload128(f < 2 ? mg : mu, splane + static_cast<uint32_t>(brow[f]) * nbk + 16u * q);
   };
-  u32x4 bq[4], sg[4], sgn[4];
+  u32x4 bq[4], sg[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
     bq[f] = bload128(f < 2 ? mg : mu, (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(g)) * 16u);
@@ -360,14 +362,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
   a_load(t, xb, xsb, src, H, 0);
   a_store(t, at[0], asc[0]);
   __syncthreads();
+#pragma unroll 1
   for (int s4 = 0; s4 < S; s4 += 4) {
-    if (s4 + 4 < S) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) sgn[f] = scale_group(f, s4 / 4 + 1);
-    }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int s = s4 + d;
+      // this step's scale bytes; on the group's last step the next group
+      // is loaded in place (its first use is one step away)
+      uint32_t sb[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        sb[f] = ((d == 0 ? sg[f].x : d == 1 ? sg[f].y : d == 2 ? sg[f].z : sg[f].w) >> (8 * g)) & 0xFFu;
+      if (d == 3 && s4 + 4 < S) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) sg[f] = scale_group(f, s4 / 4 + 1);
+      }
       u32x4 bn[4];
       if (s + 1 < S) {
         a_load(t, xb, xsb, src, H, s + 1);
@@ -382,10 +391,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
           uint32_t sa;
           const v8i af = a_frag(at[s & 1], asc[s & 1], rt, j, g, sa);
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
-            const uint32_t sw = d == 0 ? sg[f].x : d == 1 ? sg[f].y : d == 2 ? sg[f].z : sg[f].w;
-            acc[rt][f] = mfma_mx(af, bq[f], acc[rt][f], sa, (sw >> (8 * g)) & 0xFFu);
-          }
+          for (int f = 0; f < 4; ++f) acc[rt][f] = mfma_mx(af, bq[f], acc[rt][f], sa, sb[f]);
         }
       }
       if (s + 1 < S) {
@@ -395,8 +401,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
       }
       __syncthreads();
     }
-#pragma unroll
-    for (int f = 0; f < 4; ++f) sg[f] = sgn[f];
   }
   // epilogue: SwiGLU, h stored as f16 (round to nearest even)
 #pragma unroll
@@ -465,31 +469,58 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[rt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-  WFrag bf[4];
+  // codes one K-step ahead; scales two K-steps at a time (one aligned 8-byte
+  // load per row, lane group g using byte g of dword s % 2)
+  static_assert(S % 2 == 0, "scales are loaded two K-steps at a time");
+  const uint32_t nbk = static_cast<uint32_t>(I / 32), splane = static_cast<uint32_t>(H) * nbk * 16u;
+  auto scale_group = [&](int f, int q) {
+    return bload64(md, splane + static_cast<uint32_t>(c0 + 16 * f + j) * nbk + 8u * q);
+  };
+  auto codes = [&](int f, int s) {
+    return bload128(md, (static_cast<uint32_t>(c0 + 16 * f + j) * nbk + static_cast<uint32_t>(4 * s + g)) * 16u);
+  };
+  u32x4 bq[4];
+  u32x2 sg[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bf[f] = load_wfrag(md, H, I, c0 + 16 * f + j, 0, g);
+  for (int f = 0; f < 4; ++f) {
+    bq[f] = codes(f, 0);
+    sg[f] = scale_group(f, 0);
+  }
   u32x4 hv[4];
   h_load(0, hv);
   h_store(0, hv);
   __syncthreads();
-  for (int s = 0; s < S; ++s) {
-    WFrag bn[4];
+#pragma unroll 1
+  for (int s2 = 0; s2 < S; s2 += 2) {
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const int s = s2 + d;
+    float sc[4];   // this step's scales; the next pair is loaded in place on the second step
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const uint32_t sw = d == 0 ? sg[f].x : sg[f].y;
+      sc[f] = __builtin_ldexpf(1.0f, static_cast<int>((sw >> (8 * g)) & 0xFFu) - 127);
+    }
+    if (d == 1 && s2 + 2 < S) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sg[f] = scale_group(f, s2 / 2 + 1);
+    }
+    u32x4 bn[4];
     if (s + 1 < S) {
       h_load(s + 1, hv);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = load_wfrag(md, H, I, c0 + 16 * f + j, s + 1, g);
+      for (int f = 0; f < 4; ++f) bn[f] = codes(f, s + 1);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v8h b[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint32_t w = bf[f].q[q];
-        const float sc = __builtin_ldexpf(1.0f, static_cast<int>(bf[f].s) - 127);
-        const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 0);
-        const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 1);
-        const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 2);
-        const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, 3);
+        const uint32_t w = bq[f][q];
+        const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 0);
+        const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 1);
+        const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 2);
+        const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 3);
         b[f] = v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
       }
 #pragma unroll
@@ -504,9 +535,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
     if (s + 1 < S) {
       h_store((s + 1) & 1, hv);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) bf[f] = bn[f];
+      for (int f = 0; f < 4; ++f) bq[f] = bn[f];
     }
     __syncthreads();
+  }
   }
 #pragma unroll
   for (int rt = 0; rt < kRowTiles; ++rt) {
