@@ -1417,12 +1417,29 @@ int item_grid(int upper, int cap = kMaxGrid) { return upper < cap ? upper : cap;
 // several each); the others are free for routed gate/up items at once
 constexpr int kSharedWorkers = 576;
 
+// Workgroups of k_layer<S> the device holds at once: the occupancy the
+// runtime reports for its registers and LDS, times the compute units.  Kept
+// per device (a lookup once per device and shape; racing first calls compute
+// the same value).  0 on failure.
+template <class S>
 int fused_workers() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  return MOE_WAVES_PER_EU * cus;
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < kMaxDev) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dev::k_layer<S>, dev::kThreads, S::LDS_LAYER) !=
+          hipSuccess || per_cu <= 0)
+    return 0;
+  const int n = per_cu * cus;
+  if (dev >= 0 && dev < kMaxDev) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 // Tags of fused calls: unique in the process, so no word a workspace holds
@@ -1440,6 +1457,8 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
                  hipStream_t s, void* const* events, int n_events) {
   const int n_routed = rows * d->top_k;
   const bool sh = a.shared != nullptr;
+  const int workers = fused_workers<S>();
+  if (workers <= 0) return MOE_EDEVICE;
   a.tag = next_tag();
   a.err = reinterpret_cast<uint32_t*>(w8 + l.err);
   a.part_t = reinterpret_cast<uint64_t*>(w8 + l.part_t);
@@ -1449,7 +1468,7 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   a.shared_early = 1;     // the shared gate/up tiles are taken by the workers before the selection
   a.base_b = d->n_experts + rows;
   a.nb = item_grid((sh ? S::MAX_TILES_GU : 0) + n_routed * S::MAX_TILES_GU + (n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN,
-                   fused_workers());
+                   workers);
   a.base_y = a.base_b + a.nb;
   a.nsw = item_grid(kSharedWorkers, a.nb);
   const int ny = (rows * S::kH + dev::kThreads - 1) / dev::kThreads;

@@ -49,8 +49,10 @@
  *     asynchronous on it; nothing synchronises the host.  Device faults surface
  *     at the caller's next synchronisation.
  *   - The library's only mutable global state is a thread-safe counter that
- *     gives every moe_layer call a process-unique tag.  Calls on different
- *     streams with different workspaces may run concurrently.
+ *     gives every moe_layer call a process-unique tag, and per device the
+ *     number of fused-layer workgroups the device holds at once (looked up
+ *     on the first call).  Calls on different streams with different
+ *     workspaces may run concurrently.
  */
 #ifndef BIT_MOE_H
 #define BIT_MOE_H
@@ -216,10 +218,10 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
  * down items), then a fixed-order combine.  The shared expert streams while
  * the selection is made and down weights stream while h is still being
  * computed.  idx and wts are outputs as in moe_route.
- * The launch holds at most one residency round of workers (sized from the
- * device's compute-unit count), since a down item may wait on a gate/up item
- * of any worker: a kernel on another stream that keeps compute units busy
- * meanwhile can only delay it.  Should a hand-off ever fail to arrive, its
+ * The launch holds at most one residency round of workers (the occupancy the
+ * runtime reports for the kernel, times the compute units), since a down item
+ * may wait on a gate/up item of any worker: a kernel on another stream that
+ * keeps compute units busy meanwhile can only delay it.  Should a hand-off ever fail to arrive, its
  * waits end after a bounded spin and y comes out NaN. */
 int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, const void* weights, const moe_expert_ref* experts,
