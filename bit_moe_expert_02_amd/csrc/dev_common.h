@@ -131,40 +131,24 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// A double moved across lanes by one DPP pattern; lanes of rows left out by
-// ROWMASK keep their own value.
+// One step of an unsigned max across lanes: lanes of rows outside ROWMASK, or
+// whose source lane does not exist, take 0, the identity of the max.
 template <int CTRL, int ROWMASK>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = static_cast<uint32_t>(b), hi = static_cast<uint32_t>(b >> 32);
-  const uint32_t ol = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
-  const uint32_t oh = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(oh) << 32) | ol);
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, ROWMASK, 0xF, false);
+  return v > o ? v : o;
 }
-// Wave-wide max of a double, NaN operands passed over; every lane gets it.
-// Four in-row steps (quad swaps, half-row and row mirrors), then the row
-// broadcasts of lanes 15 and 31 carry the rows' maxima into row 3, whose
-// lane 63 holds the wave's.
-__device__ __forceinline__ double wave_max_f64(double v) {
-  v = __builtin_fmax(v, dpp_f64<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
-  v = __builtin_fmax(v, dpp_f64<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
-  v = __builtin_fmax(v, dpp_f64<0x141, 0xF>(v));   // row_half_mirror
-  v = __builtin_fmax(v, dpp_f64<0x140, 0xF>(v));   // row_mirror
-  v = __builtin_fmax(v, dpp_f64<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
-  v = __builtin_fmax(v, dpp_f64<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
-  const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(b), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(b >> 32), 63);
-  return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-}
-
+// Wave-wide max of a u32; every lane gets it.  Four in-row steps (quad
+// swaps, half-row and row mirrors), then the row broadcasts of lanes 15 and 31
+// carry the rows' maxima into row 3, whose lane 63 holds the wave's.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint32_t w = static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64));
-    v = v > w ? v : w;
-  }
-  return v;
+  v = dpp_max_u32<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_max_u32<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_max_u32<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_max_u32<0x140, 0xF>(v);   // row_mirror
+  v = dpp_max_u32<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_u32<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // Loads that read what other workgroups published in this kernel (through

@@ -944,37 +944,59 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
                                            const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
                                            const moe_expert_ref* refs) {
   const int lane = tid() & 63;
-  // selection keys as doubles: NaN marks an entry past E or already taken (the
-  // max instruction passes over NaN operands); a NaN key of a real expert
-  // becomes -inf so that it can still be chosen
-  double kd[kSelQ];
+  // selection keys: the double key mapped to an unsigned 64-bit integer of
+  // the same order (a NaN key of a real expert counts as -inf, -0 as +0),
+  // held as 32-bit halves.  Every real key has a nonzero upper half, so 0
+  // marks an entry past E or already taken.
+  uint32_t kh[kSelQ], kl[kSelQ];
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q) {
     const int e = lane + 64 * q;
     double key = (lv[q] + static_cast<double>(bias[q])) + 0.0;   // -0 -> +0
     key = key == key ? key : -INFINITY;
-    kd[q] = e < a.E ? key : __builtin_nan("");
+    uint64_t b = __builtin_bit_cast(uint64_t, key);
+    b = (b >> 63) ? ~b : (b | (1ull << 63));
+    kh[q] = e < a.E ? static_cast<uint32_t>(b >> 32) : 0u;
+    kl[q] = e < a.E ? static_cast<uint32_t>(b) : 0u;
   }
   int my_id = 0;         // lane j ends with the j-th selection
   for (int j = 0; j < a.k; ++j) {
-    double m = kd[0];
+    // the largest upper half; only when several entries share it do the
+    // lower halves of those entries decide
+    uint32_t mh = kh[0];
 #pragma unroll
-    for (int q = 1; q < kSelQ; ++q) m = __builtin_fmax(m, kd[q]);
-    m = wave_max_f64(m);
+    for (int q = 1; q < kSelQ; ++q) mh = mh > kh[q] ? mh : kh[q];
+    mh = wave_max_u32(mh);
+    uint64_t bq[kSelQ];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kSelQ; ++q) {
+      bq[q] = __ballot(kh[q] == mh);
+      cnt += __popcll(bq[q]);
+    }
+    if (cnt > 1) {
+      uint32_t ml = 0;
+#pragma unroll
+      for (int q = 0; q < kSelQ; ++q) {
+        const uint32_t v = kh[q] == mh ? kl[q] : 0u;
+        ml = ml > v ? ml : v;
+      }
+      ml = wave_max_u32(ml);
+#pragma unroll
+      for (int q = 0; q < kSelQ; ++q) bq[q] = __ballot(kh[q] == mh && kl[q] == ml);
+    }
     // the lowest id holding the maximum: the lowest q with a match, then the
     // lowest lane of it (ids are lane + 64 q)
     uint64_t bm = 0;
     int wq = 0;
 #pragma unroll
     for (int q = kSelQ - 1; q >= 0; --q) {
-      const uint64_t b = __ballot(kd[q] == m);
-      wq = b ? q : wq;
-      bm = b ? b : bm;
+      wq = bq[q] ? q : wq;
+      bm = bq[q] ? bq[q] : bm;
     }
     const int owner = static_cast<int>(__builtin_ctzll(bm));
 #pragma unroll
-    for (int q = 0; q < kSelQ; ++q)
-      kd[q] = (q == wq && lane == owner) ? __builtin_nan("") : kd[q];   // taken
+    for (int q = 0; q < kSelQ; ++q) kh[q] = (q == wq && lane == owner) ? 0u : kh[q];   // taken
     my_id = lane == j ? owner + 64 * wq : my_id;
   }
   // the unbiased logit of each lane's selection, fetched from the lane that
