@@ -51,7 +51,14 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 64;               // pairs of one expert per work item
 constexpr int kRowTiles = kChunk / 16;   // 16-row matrix-core tiles per chunk
 constexpr int kStepK = 128;              // K per matrix-core instruction
-constexpr int kGuCh = 128;               // gate/up channels per work item (4 waves x 32)
+// LDS row pitch of the staged activation tiles: one 16-byte slot more than a
+// row, so the 16 rows that one lane group reads per fragment start in
+// different banks (an unpadded 128- or 256-byte pitch maps them all to the
+// same banks)
+constexpr int kAPitch = kStepK + 16;     // fp8 codes, bytes
+constexpr int kHPitch = kStepK + 8;      // f16 values
+constexpr int kGuThreads = 512;          // gate/up workgroup: 8 waves
+constexpr int kGuCh = kGuThreads / 2;    // gate/up channels per work item (8 waves x 32)
 constexpr int kDnCh = 256;               // down outputs per work item (4 waves x 64)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -272,17 +279,21 @@ __device__ __forceinline__ float row16_max(float v) {
 }
 
 // The activation tile of one K-step: kChunk rows x 128 fp8 codes + 4 scale
-// bytes per row, staged in LDS by all threads (two 16-byte chunks each).
+// bytes per row, staged in LDS by all T threads of the workgroup (16-byte
+// chunks, kChunk * 8 / T each).
+template <int T>
 struct ATile {
-  u32x4 v[2];
+  static constexpr int N = kChunk * 8 / T;
+  u32x4 v[N];
   uint32_t sc;
 };
-__device__ __forceinline__ void a_load(ATile& t, const Buf& codes, const Buf& scales, const int* src,
+template <int T>
+__device__ __forceinline__ void a_load(ATile<T>& t, const Buf& codes, const Buf& scales, const int* src,
                                        int K, int s) {
   constexpr uint32_t kNone = 0x7FFFFFF0u;   // past every buffer: reads as zeros
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = threadIdx.x + kThreads * i, row = q >> 3, part = q & 7;
+  for (int i = 0; i < ATile<T>::N; ++i) {
+    const int q = threadIdx.x + T * i, row = q >> 3, part = q & 7;
     const int r = src[row];
     const uint32_t off = r >= 0 ? static_cast<uint32_t>(r) * K + s * kStepK + part * 16 : kNone;
     t.v[i] = bload128(codes, off);
@@ -292,16 +303,17 @@ __device__ __forceinline__ void a_load(ATile& t, const Buf& codes, const Buf& sc
     t.sc = r >= 0 ? dev::bload32(scales, static_cast<uint32_t>(r) * (K / 32) + 4 * s) : 0u;
   }
 }
-__device__ __forceinline__ void a_store(const ATile& t, uint8_t (*codes)[kStepK], uint32_t* sc) {
+template <int T>
+__device__ __forceinline__ void a_store(const ATile<T>& t, uint8_t (*codes)[kAPitch], uint32_t* sc) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = threadIdx.x + kThreads * i, row = q >> 3, part = q & 7;
+  for (int i = 0; i < ATile<T>::N; ++i) {
+    const int q = threadIdx.x + T * i, row = q >> 3, part = q & 7;
     *reinterpret_cast<u32x4*>(&codes[row][part * 16]) = t.v[i];
   }
   if (threadIdx.x < kChunk) sc[threadIdx.x] = t.sc;
 }
 // The lane's A fragment of row tile rt (16 rows) from the staged tile.
-__device__ __forceinline__ v8i a_frag(const uint8_t (*codes)[kStepK], const uint32_t* sc, int rt,
+__device__ __forceinline__ v8i a_frag(const uint8_t (*codes)[kAPitch], const uint32_t* sc, int rt,
                                       int j, int g, uint32_t& sa) {
   const int row = rt * 16 + j;
   const u32x4 lo = *reinterpret_cast<const u32x4*>(&codes[row][16 * g]);
@@ -311,17 +323,32 @@ __device__ __forceinline__ v8i a_frag(const uint8_t (*codes)[kStepK], const uint
              static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
 }
 
-// gate/up: work item (chunk, 128 channels); wave w owns channels c0 .. c0+31
-// of gate and up (four B fragments per K-step), every row tile of the chunk.
+// Work items that share a chunk's activation tile go to one XCD.  The
+// dispatcher hands workgroups to the eight XCDs round-robin by id, so item
+// (chunk ci, tile nt) takes id 8 * ((ci / 8) * NT + nt) + ci % 8: the NT tiles
+// of chunk ci run back to back on XCD ci % 8, whose L2 then holds the tile.
+constexpr int kXcd = 8;
+__device__ __forceinline__ void item_of_block(int b, int NT, int& ci, int& nt) {
+  const int x = b % kXcd, l = b / kXcd;
+  nt = l % NT;
+  ci = (l / NT) * kXcd + x;
+}
+
+// gate/up: work item (chunk, 256 channels); wave w of eight owns channels
+// c0 .. c0+31 of gate and up (four B fragments per K-step), every row tile of
+// the chunk.  The eight waves share one staged activation tile, so a chunk's
+// activations are read by I / 256 workgroups.
 // h = silu(G) * V is quantised to MXFP8 per (row, 32 channels) -- exactly the
 // wave's channels -- and stored at the pairs' expert-sorted positions.
 template <int H, int I>
-__global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
+__global__ __launch_bounds__(kGuThreads, 1) void k_gateup(Args a) {
   constexpr int NT = I / kGuCh, S = H / kStepK;
-  __shared__ __align__(16) uint8_t at[2][kChunk][kStepK];
+  static_assert(I % kGuCh == 0, "whole channel tiles");
+  __shared__ __align__(16) uint8_t at[2][kChunk][kAPitch];
   __shared__ uint32_t asc[2][kChunk];
   __shared__ int src[kChunk];
-  const int ci = blockIdx.x / NT, nt = blockIdx.x - ci * NT;
+  int ci, nt;
+  item_of_block(blockIdx.x, NT, ci, nt);
   if (ci >= uniform(*a.n_chunks)) return;
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
@@ -343,62 +370,75 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
   for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[rt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-  // Weight codes one K-step ahead; their e8m0 scales four K-steps at a time:
-  // the 16 scale bytes of a row for steps 4q .. 4q+3 are one aligned 16-byte
-  // load shared by the row's four lane groups (lane group g uses byte g of
-  // dword s % 4), instead of a one-byte load per fragment and step.
+  // Software pipeline over the K-steps:
+  //   weight codes   a lane's 16-byte pieces of steps 2t and 2t+1 are the two
+  //                  halves of one 128-byte line: both are loaded together,
+  //                  on step 2t-2, into a ring of four steps.  Loaded a step
+  //                  apart, a line could leave L2 between its halves and be
+  //                  fetched twice
+  //   e8m0 scales    four K-steps per aligned 16-byte load of the row (lane
+  //                  group g uses byte g of dword s % 4), a group ahead
+  //   activations    two steps ahead into registers, stored to the LDS
+  //                  double buffer one step before use
+  // Within a step the loads go out in the order of their use, so the wait
+  // for one never drains a load needed later (the counter is in order).
   static_assert(S % 4 == 0, "scales are loaded four K-steps at a time");
+  constexpr int kRing = 4;
   const uint32_t nbk = static_cast<uint32_t>(H / 32), splane = static_cast<uint32_t>(I) * nbk * 16u;
   auto scale_group = [&](int f, int q) {
     return bload128(f < 2 ? mg : mu, splane + static_cast<uint32_t>(brow[f]) * nbk + 16u * q);
   };
-  u32x4 bq[4], sg[4];
+  auto codes = [&](int f, int s) {
+    return bload128(f < 2 ? mg : mu, (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(4 * s + g)) * 16u);
+  };
+  u32x4 bq[kRing][4], sg[2][4];
+  ATile<kGuThreads> ta[2];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    bq[f] = bload128(f < 2 ? mg : mu, (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(g)) * 16u);
-    sg[f] = scale_group(f, 0);
-  }
-  ATile t;
-  a_load(t, xb, xsb, src, H, 0);
-  a_store(t, at[0], asc[0]);
+  for (int f = 0; f < 4; ++f) sg[0][f] = scale_group(f, 0);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bq[p][f] = codes(f, p);
+  a_load(ta[0], xb, xsb, src, H, 0);
+  if (S > 1) a_load(ta[1], xb, xsb, src, H, 1);
+  a_store(ta[0], at[0], asc[0]);
   __syncthreads();
+  // eight steps per iteration: every ring index is a compile-time constant
 #pragma unroll 1
-  for (int s4 = 0; s4 < S; s4 += 4) {
+  for (int s8 = 0; s8 < S; s8 += 8) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int s = s4 + d;
-      // this step's scale bytes; on the group's last step the next group
-      // is loaded in place (its first use is one step away)
+    for (int d = 0; d < 8; ++d) {
+      const int s = s8 + d;
+      if (S % 8 != 0 && s >= S) break;
+      const int gq = d / 4;   // scale group slot of this step
+      if (d % 4 == 0 && s + 4 < S) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) sg[gq ^ 1][f] = scale_group(f, s / 4 + 1);
+      }
+      if (s + 2 < S) a_load(ta[d % 2], xb, xsb, src, H, s + 2);
+      if (d % 2 == 0 && s + 2 < S) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          bq[(d + 2) % kRing][f] = codes(f, s + 2);
+          bq[(d + 3) % kRing][f] = codes(f, s + 3);
+        }
+      }
       uint32_t sb[4];
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        sb[f] = ((d == 0 ? sg[f].x : d == 1 ? sg[f].y : d == 2 ? sg[f].z : sg[f].w) >> (8 * g)) & 0xFFu;
-      if (d == 3 && s4 + 4 < S) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) sg[f] = scale_group(f, s4 / 4 + 1);
-      }
-      u32x4 bn[4];
-      if (s + 1 < S) {
-        a_load(t, xb, xsb, src, H, s + 1);
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          bn[f] = bload128(f < 2 ? mg : mu,
-                           (static_cast<uint32_t>(brow[f]) * nbk + static_cast<uint32_t>(4 * (s + 1) + g)) * 16u);
+      for (int f = 0; f < 4; ++f) {
+        const u32x4 w = sg[gq][f];
+        sb[f] = ((d % 4 == 0 ? w.x : d % 4 == 1 ? w.y : d % 4 == 2 ? w.z : w.w) >> (8 * g)) & 0xFFu;
       }
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
         if (rt < mt) {
           uint32_t sa;
-          const v8i af = a_frag(at[s & 1], asc[s & 1], rt, j, g, sa);
+          const v8i af = a_frag(at[d % 2], asc[d % 2], rt, j, g, sa);
 #pragma unroll
-          for (int f = 0; f < 4; ++f) acc[rt][f] = mfma_mx(af, bq[f], acc[rt][f], sa, sb[f]);
+          for (int f = 0; f < 4; ++f) acc[rt][f] = mfma_mx(af, bq[d % kRing][f], acc[rt][f], sa, sb[f]);
         }
       }
-      if (s + 1 < S) {
-        a_store(t, at[(s + 1) & 1], asc[(s + 1) & 1]);
-#pragma unroll
-        for (int f = 0; f < 4; ++f) bq[f] = bn[f];
-      }
+      if (s + 1 < S) a_store(ta[(d + 1) % 2], at[(d + 1) % 2], asc[(d + 1) % 2]);
       __syncthreads();
     }
   }
@@ -431,9 +471,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_gateup(Args a) {
 template <int H, int I>
 __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   constexpr int NT = H / kDnCh, S = I / kStepK;
-  __shared__ __align__(16) uint16_t at[2][kChunk][kStepK];
+  __shared__ __align__(16) uint16_t at[2][kChunk][kHPitch];
   __shared__ int src[kChunk];
-  const int ci = blockIdx.x / NT, nt = blockIdx.x - ci * NT;
+  int ci, nt;
+  item_of_block(blockIdx.x, NT, ci, nt);
   if (ci >= uniform(*a.n_chunks)) return;
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
@@ -469,9 +510,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   for (int rt = 0; rt < kRowTiles; ++rt)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[rt][f] = v4f{0.f, 0.f, 0.f, 0.f};
-  // codes one K-step ahead; scales two K-steps at a time (one aligned 8-byte
-  // load per row, lane group g using byte g of dword s % 2)
+  // Software pipeline as in the gate/up kernel: the codes of steps 2t and
+  // 2t+1 (one 128-byte line) loaded together on step 2t-2 into a ring of four
+  // steps; scales two K-steps per aligned 8-byte load of the row
+  // (lane group g uses byte g of dword s % 2), a group ahead; the h tile two
+  // steps ahead into registers, stored to the LDS double buffer one step
+  // before use.  Loads go out in the order of their use.
   static_assert(S % 2 == 0, "scales are loaded two K-steps at a time");
+  constexpr int kRing = 4;
   const uint32_t nbk = static_cast<uint32_t>(I / 32), splane = static_cast<uint32_t>(H) * nbk * 16u;
   auto scale_group = [&](int f, int q) {
     return bload64(md, splane + static_cast<uint32_t>(c0 + 16 * f + j) * nbk + 8u * q);
@@ -479,44 +525,50 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   auto codes = [&](int f, int s) {
     return bload128(md, (static_cast<uint32_t>(c0 + 16 * f + j) * nbk + static_cast<uint32_t>(4 * s + g)) * 16u);
   };
-  u32x4 bq[4];
-  u32x2 sg[4];
+  u32x4 bq[kRing][4], hv[2][4];
+  u32x2 sg[2][4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    bq[f] = codes(f, 0);
-    sg[f] = scale_group(f, 0);
-  }
-  u32x4 hv[4];
-  h_load(0, hv);
-  h_store(0, hv);
+  for (int f = 0; f < 4; ++f) sg[0][f] = scale_group(f, 0);
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) bq[p][f] = codes(f, p);
+  h_load(0, hv[0]);
+  h_load(1, hv[1]);
+  h_store(0, hv[0]);
   __syncthreads();
+  // four steps per iteration: every ring index is a compile-time constant
 #pragma unroll 1
-  for (int s2 = 0; s2 < S; s2 += 2) {
+  for (int s4 = 0; s4 < S; s4 += 4) {
 #pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    const int s = s2 + d;
-    float sc[4];   // this step's scales; the next pair is loaded in place on the second step
+  for (int d = 0; d < 4; ++d) {
+    const int s = s4 + d;
+    if (S % 4 != 0 && s >= S) break;
+    const int gq = d / 2;   // scale group slot of this step
+    if (d % 2 == 0 && s + 2 < S) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sg[gq ^ 1][f] = scale_group(f, s / 2 + 1);
+    }
+    if (s + 2 < S) h_load(s + 2, hv[d % 2]);
+    if (d % 2 == 0 && s + 2 < S) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        bq[(d + 2) % kRing][f] = codes(f, s + 2);
+        bq[(d + 3) % kRing][f] = codes(f, s + 3);
+      }
+    }
+    float sc[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-      const uint32_t sw = d == 0 ? sg[f].x : sg[f].y;
+      const uint32_t sw = d % 2 == 0 ? sg[gq][f].x : sg[gq][f].y;
       sc[f] = __builtin_ldexpf(1.0f, static_cast<int>((sw >> (8 * g)) & 0xFFu) - 127);
-    }
-    if (d == 1 && s2 + 2 < S) {
-#pragma unroll
-      for (int f = 0; f < 4; ++f) sg[f] = scale_group(f, s2 / 2 + 1);
-    }
-    u32x4 bn[4];
-    if (s + 1 < S) {
-      h_load(s + 1, hv);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) bn[f] = codes(f, s + 1);
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v8h b[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        const uint32_t w = bq[f][q];
+        const uint32_t w = bq[d % kRing][f][q];
         const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 0);
         const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 1);
         const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc[f], 2);
@@ -526,17 +578,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
 #pragma unroll
       for (int rt = 0; rt < kRowTiles; ++rt) {
         if (rt < mt) {
-          const v8h af = *reinterpret_cast<const v8h*>(&at[s & 1][rt * 16 + j][32 * g + 8 * q]);
+          const v8h af = *reinterpret_cast<const v8h*>(&at[d % 2][rt * 16 + j][32 * g + 8 * q]);
 #pragma unroll
           for (int f = 0; f < 4; ++f) acc[rt][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b[f], acc[rt][f], 0, 0, 0);
         }
       }
     }
-    if (s + 1 < S) {
-      h_store((s + 1) & 1, hv);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) bq[f] = bn[f];
-    }
+    if (s + 1 < S) h_store((d + 1) % 2, hv[(d + 1) % 2]);
     __syncthreads();
   }
   }
@@ -628,9 +676,10 @@ int launch_prefill(const moe_dims* d, int rows, pf::Args a, const PfLayout& l, h
   hipLaunchKernelGGL(pf::k_quant, dim3(nb), dim3(pf::kThreads), 0, s, a.x, rows, H, a.xq, a.xs);
   hipLaunchKernelGGL(pf::k_count, dim3(d->n_experts), dim3(pf::kThreads), 0, s, a);
   hipLaunchKernelGGL(pf::k_place, dim3(d->n_experts), dim3(pf::kThreads), 0, s, a);
-  hipLaunchKernelGGL((pf::k_gateup<H, I>), dim3(l.max_chunks * (I / pf::kGuCh)), dim3(pf::kThreads), 0,
+  const int chunk_groups = (l.max_chunks + pf::kXcd - 1) / pf::kXcd;   // ids cover every chunk slot
+  hipLaunchKernelGGL((pf::k_gateup<H, I>), dim3(chunk_groups * pf::kXcd * (I / pf::kGuCh)), dim3(pf::kGuThreads), 0,
                      s, a);
-  hipLaunchKernelGGL((pf::k_down<H, I>), dim3(l.max_chunks * (H / pf::kDnCh)), dim3(pf::kThreads), 0, s,
+  hipLaunchKernelGGL((pf::k_down<H, I>), dim3(chunk_groups * pf::kXcd * (H / pf::kDnCh)), dim3(pf::kThreads), 0, s,
                      a);
   hipLaunchKernelGGL(pf::k_combine<H>, dim3((rows * H + pf::kThreads - 1) / pf::kThreads),
                      dim3(pf::kThreads), 0, s, a);
