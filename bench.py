@@ -327,6 +327,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the MI355X"
     L.lib()
+    if args.copy_calib_mb:
+        src = torch.ones(args.copy_calib_mb << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "fp4_prefill":
         bench_prefill(args, torch, L, LY, synth)
         return
@@ -338,13 +345,6 @@ def main():
     print(f"[bench] building {args.copies} layer copies of {wl.name}", file=sys.stderr, flush=True)
     layers = build_copies(wl, args.copies, args.pool)
     torch.cuda.synchronize()
-    if args.copy_calib_mb:
-        src = torch.ones(args.copy_calib_mb << 18, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     def xs_for(rows, n, base):
         return [torch.from_numpy(synth.x_bf16(wl, 0, rows, base + i).view(np.int16).copy()).cuda()
