@@ -323,15 +323,20 @@ __device__ __forceinline__ v8i a_frag(const uint8_t (*codes)[kAPitch], const uin
              static_cast<int>(hi.x), static_cast<int>(hi.y), static_cast<int>(hi.z), static_cast<int>(hi.w)};
 }
 
-// Work items that share a chunk's activation tile go to one XCD.  The
-// dispatcher hands workgroups to the eight XCDs round-robin by id, so item
-// (chunk ci, tile nt) takes id 8 * ((ci / 8) * NT + nt) + ci % 8: the NT tiles
-// of chunk ci run back to back on XCD ci % 8, whose L2 then holds the tile.
+// Work items are placed by XCD.  The dispatcher hands workgroups to the eight
+// XCDs round-robin by id, so id b runs on XCD b % 8, as the (b / 8)-th of that
+// XCD.  XCD x takes the x-th eighth of the chunk list (chunks are in expert
+// order) and walks it chunk by chunk, the NT tiles of a chunk back to back:
+// a chunk's activation tile, and the weight tile nt of an expert's
+// consecutive chunks, are read by workgroups that run together on one XCD,
+// so its L2 serves the repeats.  ci = -1: no item for this id.
 constexpr int kXcd = 8;
-__device__ __forceinline__ void item_of_block(int b, int NT, int& ci, int& nt) {
-  const int x = b % kXcd, l = b / kXcd;
+__device__ __forceinline__ void item_of_block(int b, int NT, int n_chunks, int& ci, int& nt) {
+  const int x = b % kXcd, l = b / kXcd, per = (n_chunks + kXcd - 1) / kXcd;
   nt = l % NT;
-  ci = (l / NT) * kXcd + x;
+  const int c = l / NT;
+  ci = c < per ? x * per + c : -1;
+  if (ci >= n_chunks) ci = -1;
 }
 
 // gate/up: work item (chunk, 256 channels); wave w of eight owns channels
@@ -348,8 +353,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void k_gateup(Args a) {
   __shared__ uint32_t asc[2][kChunk];
   __shared__ int src[kChunk];
   int ci, nt;
-  item_of_block(blockIdx.x, NT, ci, nt);
-  if (ci >= uniform(*a.n_chunks)) return;
+  item_of_block(blockIdx.x, NT, uniform(*a.n_chunks), ci, nt);
+  if (ci < 0) return;
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
   const moe_expert_ref ref = a.experts[uniform(ch.expert)];
@@ -474,8 +479,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   __shared__ __align__(16) uint16_t at[2][kChunk][kHPitch];
   __shared__ int src[kChunk];
   int ci, nt;
-  item_of_block(blockIdx.x, NT, ci, nt);
-  if (ci >= uniform(*a.n_chunks)) return;
+  item_of_block(blockIdx.x, NT, uniform(*a.n_chunks), ci, nt);
+  if (ci < 0) return;
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
   const moe_expert_ref ref = a.experts[uniform(ch.expert)];
