@@ -1345,15 +1345,16 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   __syncthreads();
   const int n_gu = uniform(tab.n_gu), n_dn = uniform(tab.n_dn);
   // the down list is taken from the shared expert's tiles on (they are the
-  // list's last): its h is ready long before the routed ones, so its weights
-  // stream while the routed gate/up items are still finishing
+  // list's last, from n_dn - sh_dn): its h is ready long before the routed
+  // ones, so its weights stream while the routed gate/up items are still
+  // finishing; the routed slots follow in list order
   const int sh_dn = a.shared ? uniform(tab.dn_off[ns] - tab.dn_off[ns - 1]) : 0;
   // the routed list starts at worker nsw: the workers holding shared tiles
   // get its later positions, so the routed gate/up items start on free
   // workers as soon as the selection is out
   for (int j = (w - a.nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
     if (j < n_gu) run_item<S, 2, true>(a, &tab, offs[0], ns, j, sl, lds, tag);
-    else run_item<S, 0, true>(a, &tab, offs[1], ns, (j - n_gu + sh_dn) % n_dn, sl, lds, tag);
+    else run_item<S, 0, true>(a, &tab, offs[1], ns, (j - n_gu + n_dn - sh_dn) % n_dn, sl, lds, tag);
   }
 }
 
