@@ -1277,7 +1277,12 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   stage_x_row<S>(a, 0, lds);   // before any wait: every gate/up item of row 0 finds x here
 
   const int nsh = a.shared ? uniform(tiles_of<S, true>(shref.fmt)) : 0;
-  if (w < a.nsw && w < nsh) {
+  // workers taking the shared gate/up tiles: one tile each, but at one row a
+  // tile is cheap and two each leave more workers free for the routed items
+  // when the selection comes out (a.nsw caps it)
+  const int nsw_want = a.R == 1 ? (nsh + 1) / 2 : nsh;
+  const int nsw = a.nsw < nsw_want ? a.nsw : nsw_want;
+  if (w < nsw) {
     // shared gate/up tiles need only x: they stream while the selection is
     // made.  They wait until the selection has every logit, so neither the
     // router's loads nor the selection's poll queue behind this traffic.
@@ -1293,7 +1298,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
       (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err);
     }
     __syncthreads();
-    for (int t = w; t < nsh; t += a.nsw) {
+    for (int t = w; t < nsh; t += nsw) {
       run_slot<S, 2, true>(a, sl, t, lds, tag);
       __syncthreads();   // LDS is reused next
     }
@@ -1352,7 +1357,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   // the routed list starts at worker nsw: the workers holding shared tiles
   // get its later positions, so the routed gate/up items start on free
   // workers as soon as the selection is out
-  for (int j = (w - a.nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
+  for (int j = (w - nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
     if (j < n_gu) run_item<S, 2, true>(a, &tab, offs[0], ns, j, sl, lds, tag);
     else run_item<S, 0, true>(a, &tab, offs[1], ns, (j - n_gu + n_dn - sh_dn) % n_dn, sl, lds, tag);
   }
@@ -1440,8 +1445,8 @@ int item_grid(int upper, int cap = kMaxGrid) { return upper < cap ? upper : cap;
 // Fused launch: at most one residency round of workers, so that all of them
 // can be resident at once once the router and selection workgroups are done
 // (a down item may wait on a gate/up item of any worker).
-// workers that take the shared expert's gate/up tiles (before the selection,
-// several each); the others are free for routed gate/up items at once
+// at most this many workers take the shared expert's gate/up tiles (before
+// the selection); the others are free for routed gate/up items at once
 constexpr int kSharedWorkers = 576;
 
 // Workgroups of k_layer<S> the device holds at once: the occupancy the
