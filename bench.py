@@ -157,6 +157,28 @@ def run_steps(torch, L, LY, layers, xs, rows, steps, warmup, events=None, hev=No
     return t1 - t0, per, idx[warmup:].cpu().numpy()
 
 
+def stream_read_ceiling(torch, L):
+    """The device's streaming-read rate (GB/s): the best of a few launch
+    shapes of the library's plain read kernel over 4 GiB, timed with events."""
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    best = 0.0
+    for grid, unroll in ((1024, 2), (2048, 4), (4096, 8), (8192, 8)):
+        sink = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            L.moe_stream_read(buf, nbytes, sink, grid, unroll)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        n = 10
+        for _ in range(n):
+            L.moe_stream_read(buf, nbytes, sink, grid, unroll)
+        b.record()
+        b.synchronize()
+        best = max(best, nbytes * n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
 def cpu_baseline(wl, rows):
     """The oracle, as it stands, on `rows` rows of layer copy 0, BLAS pinned to one thread."""
     from threadpoolctl import threadpool_limits
@@ -181,16 +203,23 @@ def cpu_baseline(wl, rows):
         return (OF.decode(f, g, wl.inter, wl.hidden), OF.decode(f, u, wl.inter, wl.hidden),
                 OF.decode(f, d, wl.hidden, wl.inter))
 
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        out = OM.moe_layer(x, wr, wl.top_k, expert,
-                           shared=expert(wl.n_experts) if wl.shared_fmt else None,
-                           bias=synth.bias(wl, 0))
-        t = time.perf_counter() - t0
-    assert np.array_equal(out["idx"], idx)
+    def timed(limit):
+        with threadpool_limits(limits=limit):
+            t0 = time.perf_counter()
+            out = OM.moe_layer(x, wr, wl.top_k, expert,
+                               shared=expert(wl.n_experts) if wl.shared_fmt else None,
+                               bias=synth.bias(wl, 0))
+            t = time.perf_counter() - t0
+        assert np.array_equal(out["idx"], idx)
+        return t
+
+    t = timed(1)
+    ncores = len(os.sched_getaffinity(0))
+    t_all = timed(ncores)
     return dict(value=round(rows / t, 4), unit="tokens/s", cores=1, kind="oracle",
                 sample=f"{rows} row(s) of one decode_q2 layer (route + decode of the selected "
-                       f"experts and the shared expert + fp64 math), {t:.2f} s, BLAS 1 thread")
+                       f"experts and the shared expert + fp64 math), {t:.2f} s, BLAS 1 thread",
+                all_cores=dict(value=round(rows / t_all, 4), cores=ncores, seconds=round(t_all, 2)))
 
 
 def bench_prefill(args, torch, L, LY, synth):
@@ -368,6 +397,8 @@ def main():
               f"{np.round(per.mean(axis=0) * 1e3, 2).tolist()}",
               file=sys.stderr, flush=True)
 
+    ceiling = stream_read_ceiling(torch, L)
+    print(f"[bench] streaming-read ceiling {ceiling:.0f} GB/s", file=sys.stderr, flush=True)
     r = results[args.rows]
     ms_step = r["secs"] / args.steps * 1e3
     value = args.rows * args.steps / r["secs"]
@@ -400,6 +431,10 @@ def main():
             "layer_GBps": round(layer_gbps, 1),
             "layer_frac_of_hbm_peak": round(layer_gbps / HBM_PEAK_GBPS, 4),
             "kernel_us": {name: round(float(r["per"][:, j].mean()) * 1e3, 3) for j, name in enumerate(KERNELS)},
+            "kernel_us_p10_p50_p90": [round(float(v) * 1e3, 3)
+                                      for v in np.percentile(r["per"][:, 0], [10, 50, 90])],
+            "stream_read_ceiling_GBps": round(ceiling, 1),
+            "layer_frac_of_stream_ceiling": round(layer_gbps / ceiling, 4),
             "rows_sweep": {str(k): {"tokens_per_s": round(k * args.steps / v["secs"], 1),
                                     "us_per_step": round(v["secs"] / args.steps * 1e6, 2),
                                     "unique_experts": round(v["uniq"], 2),
@@ -417,6 +452,8 @@ def main():
             "kernel": "k_layer (the whole layer in one launch)",
             "bytes_per_launch": int(fused_bytes),
             "avg_launch_us": round(b_ms * 1e3, 3),
+            "stream_ceiling": round(ceiling, 1),
+            "frac_of_stream_ceiling": round(achieved / ceiling, 4),
         },
         "cpu_baseline": None,
     }

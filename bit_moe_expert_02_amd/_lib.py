@@ -23,7 +23,8 @@ MAX_TOP_K = 8
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
-           "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8")
+           "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
+           "moe_stream_read")
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,8 @@ def lib():
                                          vp, vp, i32]
         L.moe_quant_mxfp8.restype = ctypes.c_int
         L.moe_quant_mxfp8.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_stream_read.restype = ctypes.c_int
+        L.moe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
@@ -210,3 +213,9 @@ def moe_stack_decode(d, layers, rows, x_all, noise, y_all, idx_all, wts_all, ws,
 def moe_quant_mxfp8(x, rows, k, codes, scales, stream=None):
     _check("moe_quant_mxfp8", lib().moe_quant_mxfp8(_ptr(x), int(rows), int(k), _ptr(codes),
                                                     _ptr(scales), _stream(stream)))
+
+
+def moe_stream_read(buf, nbytes, sink, grid, unroll, stream=None):
+    """Measurement aid: the streaming-read kernel over the first nbytes of buf."""
+    _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(grid),
+                                                    int(unroll), _stream(stream)))

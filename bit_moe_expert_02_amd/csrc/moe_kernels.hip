@@ -1377,6 +1377,29 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   a.y[i] = s;
 }
 
+// Streaming-read ceiling: every lane reads U 16-byte chunks per iteration,
+// grid-striding, and folds them into an xor checksum.
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4* __restrict__ p, size_t n16,
+                                                         uint32_t* sink) {
+  const size_t nth = static_cast<size_t>(gridDim.x) * kThreads;
+  const size_t t = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  const size_t rounds = n16 / (U * nth);   // whole rounds; the rest is the tail
+  for (size_t m = 0, i = t; m < rounds; ++m, i += U * nth) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * nth);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (size_t i = t + rounds * U * nth; i < n16; i += nth) {   // the tail
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[t] = acc;
+}
+
 }  // namespace dev
 
 // ===========================================================================
@@ -1645,6 +1668,24 @@ const char* moe_status_string(int status) {
     case MOE_ECODE: return "invalid packed code";
     default: return "unknown status";
   }
+}
+
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll,
+                    void* stream) {
+  if (!buf || !sink || (reinterpret_cast<uintptr_t>(buf) & 15u) || grid < 1 || grid > 65536)
+    return MOE_EINVAL;
+  const auto* p = static_cast<const moe::dev::u32x4*>(buf);
+  const size_t n16 = bytes / 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 g(static_cast<unsigned>(grid)), b(moe::dev::kThreads);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(moe::dev::k_stream_read<1>, g, b, 0, s, p, n16, sink); break;
+    case 2: hipLaunchKernelGGL(moe::dev::k_stream_read<2>, g, b, 0, s, p, n16, sink); break;
+    case 4: hipLaunchKernelGGL(moe::dev::k_stream_read<4>, g, b, 0, s, p, n16, sink); break;
+    case 8: hipLaunchKernelGGL(moe::dev::k_stream_read<8>, g, b, 0, s, p, n16, sink); break;
+    default: return MOE_EINVAL;
+  }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows) {

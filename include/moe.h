@@ -266,6 +266,26 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
                      int32_t rows, void* x_all, const float* noise, float* y_all,
                      int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement aid (not a step of the method).                               */
+/* ------------------------------------------------------------------------ */
+
+/* The streaming-read ceiling against which the layer's HBM rate is also
+ * reported ("DeepSeek-V4.1-Flash served three ways on 4xL20", section 7: a
+ * bandwidth figure is judged against what the device reaches on a plain
+ * stream).  Reads the first floor(bytes / 16) 16-byte chunks of `buf` with
+ * one 16-byte load per lane and `unroll` loads in flight per lane per
+ * iteration, grid-striding over `grid` workgroups of 256 threads, and
+ * writes one xor checksum per thread to `sink` so that no load is dropped.
+ *   buf      device, 16-byte aligned, read-only
+ *   sink     device, grid * 256 uint32, out (contents are only a checksum)
+ *   grid     1 .. 65536 workgroups;  unroll  1, 2, 4 or 8
+ * Asynchronous on `stream`; time it with events.  MOE_EINVAL on a null or
+ * misaligned pointer or an argument out of range, MOE_EDEVICE if the launch
+ * fails. */
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif
