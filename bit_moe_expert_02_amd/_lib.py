@@ -24,7 +24,7 @@ MAX_TOP_K = 8
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
            "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
-           "moe_stream_read")
+           "moe_stream_read", "moe_set_spin_limit")
 
 
 class MoeError(RuntimeError):
@@ -88,6 +88,8 @@ def lib():
                                          vp, vp, i32]
         L.moe_quant_mxfp8.restype = ctypes.c_int
         L.moe_quant_mxfp8.argtypes = [vp, i32, i32, vp, vp, vp]
+        L.moe_set_spin_limit.restype = ctypes.c_int32
+        L.moe_set_spin_limit.argtypes = [i32]
         L.moe_stream_read.restype = ctypes.c_int
         L.moe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
         L.moe_stack_decode.restype = ctypes.c_int
@@ -219,3 +221,11 @@ def moe_stream_read(buf, nbytes, sink, grid, unroll, stream=None):
     """Measurement aid: the streaming-read kernel over the first nbytes of buf."""
     _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(grid),
                                                     int(unroll), _stream(stream)))
+
+
+def moe_set_spin_limit(polls):
+    """Polls before a hand-off wait of the fused launch gives up; returns the previous limit."""
+    prev = lib().moe_set_spin_limit(int(polls))
+    if prev < 0:
+        raise MoeError("moe_set_spin_limit", prev)
+    return prev

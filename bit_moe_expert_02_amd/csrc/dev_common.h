@@ -162,7 +162,7 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // tag is per call (an epoch kept in the workspace), so words left by earlier
 // calls never look ready.
 // ---------------------------------------------------------------------------
-constexpr int kSpinLimit = 1 << 16;   // polls before a wait gives up (tens of ms)
+constexpr int kSpinLimit = 1 << 16;   // default polls before a wait gives up (tens of ms)
 
 __device__ __forceinline__ uint64_t tload(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -173,10 +173,13 @@ __device__ __forceinline__ void tstore(uint64_t* p, uint32_t tag, uint32_t v) {
 }
 // N words at once: addr(j) gives word j's address, or null for none (then its
 // payload reads 0).  All loads are issued together; only the words not yet
-// carrying `tag` are polled again.  Payloads land in out[].
+// carrying `tag` are polled again.  Payloads land in out[].  After `limit`
+// polls the wait ends, *err is set to `tag` and false is returned (the
+// payloads of the words that never came are stale).
 template <int N, class AddrF>
-__device__ __forceinline__ void await_batch(AddrF addr, uint32_t tag, uint32_t* err,
-                                            uint32_t (&out)[N]) {
+__device__ __forceinline__ bool await_batch(AddrF addr, uint32_t tag, uint32_t* err,
+                                            uint32_t (&out)[N], int limit) {
+  bool all = true;
   uint64_t w[N];
   const uint64_t ready0 = static_cast<uint64_t>(tag) << 32;
 #pragma unroll
@@ -185,11 +188,11 @@ __device__ __forceinline__ void await_batch(AddrF addr, uint32_t tag, uint32_t* 
     w[j] = p ? tload(p) : ready0;
   }
   for (int it = 0;; ++it) {
-    bool all = true;
+    all = true;
 #pragma unroll
     for (int j = 0; j < N; ++j) all = all && static_cast<uint32_t>(w[j] >> 32) == tag;
     if (all) break;
-    if (it >= kSpinLimit) {
+    if (it >= limit) {
       __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
@@ -200,13 +203,15 @@ __device__ __forceinline__ void await_batch(AddrF addr, uint32_t tag, uint32_t* 
   }
 #pragma unroll
   for (int j = 0; j < N; ++j) out[j] = static_cast<uint32_t>(w[j]);
+  return all;
 }
 
-// Payload of *p once it carries `tag`.  After kSpinLimit polls the wait ends,
+// Payload of *p once it carries `tag`.  After `limit` polls the wait ends,
 // *err is set to `tag` and 0 is returned: a launch always drains, and the
 // failure is recorded for that call in the error word.
-__device__ __forceinline__ uint32_t await_word(const uint64_t* p, uint32_t tag, uint32_t* err) {
-  for (int i = 0; i < kSpinLimit; ++i) {
+__device__ __forceinline__ uint32_t await_word(const uint64_t* p, uint32_t tag, uint32_t* err,
+                                               int limit) {
+  for (int i = 0; i < limit; ++i) {
     const uint64_t w = tload(p);
     if (static_cast<uint32_t>(w >> 32) == tag) return static_cast<uint32_t>(w);
     __builtin_amdgcn_s_sleep(8);

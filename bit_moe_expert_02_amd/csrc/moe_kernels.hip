@@ -112,6 +112,7 @@ struct Args {
   // hand-off words and the layout of the workgroup roles
   uint32_t tag;                   // this call's tag: unique in the process (never 0)
   uint32_t* err;                  // [1] the tag of a call in which a wait gave up
+  int spin_limit;                 // polls before a hand-off wait gives up
   uint64_t* part_t;               // [(R*k + R) x H] partial outputs as tagged fp32
   uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
   uint64_t* selt;                 // kSelRep copies of [R x k x kSelWords] selection entries
@@ -629,14 +630,14 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
         const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
         // first a sparse wait (one word in every I/kThreads, which samples
         // every gate/up tile of 16 channels), then the whole vector once
-        (void)await_word(src + (tid() * (I / kThreads)), tag, a.err);
+        (void)await_word(src + (tid() * (I / kThreads)), tag, a.err, a.spin_limit);
         uint32_t v[PER];
         await_batch<PER>(
             [src](int j) -> const uint64_t* {
               const int i = tid() + j * kThreads;
               return i < I ? src + i : nullptr;
             },
-            tag, a.err, v);
+            tag, a.err, v, a.spin_limit);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
           const int i = tid() + j * kThreads;
@@ -931,7 +932,7 @@ __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel
         const int e = lane + 64 * (j >> 1);
         return e < E ? lg + 2 * e + (j & 1) : nullptr;
       },
-      tag, a.err, half);
+      tag, a.err, half, a.spin_limit);
   if (r == 0 && a.selt && lane < kSelRep) tstore(a.selt + lane * kSelRepWords + kSelEntryWords, tag, 1u);
   double lv[kSelQ];
 #pragma unroll
@@ -1187,7 +1188,7 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
         if (q < k) return part + static_cast<size_t>(r * k + q) * S::kH + n;
         return (q == kMaxK && sh) ? part + static_cast<size_t>(R * k + r) * S::kH + n : nullptr;
       },
-      tag, a.err, w);
+      tag, a.err, w, a.spin_limit);
   int id[kMaxK], rank[kMaxK];
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) id[j] = j < k ? static_cast<int>(w[j] & 0xFFFFu) : 0x7fffffff;
@@ -1295,7 +1296,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
         sl.pair[r] = a.R * a.k + r;
         sl.w[r] = 1.0f;
       }
-      (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err);
+      (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err, a.spin_limit);
     }
     __syncthreads();
     for (int t = w; t < nsh; t += nsw) {
@@ -1318,14 +1319,26 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     constexpr int PER = kSelEntryWords / 64;
     const int lane = tid();
     uint32_t v[PER];
-    await_batch<PER>(
+    const bool got = await_batch<PER>(
         [selt = a.selt + (bid % kSelRep) * kSelRepWords, lim = n * kSelWords, lane](int j) -> const uint64_t* {
           const int i = lane + j * 64;
           return i < lim ? selt + i : nullptr;
         },
-        tag, a.err, v);
+        tag, a.err, v, a.spin_limit);
+    // a wait that gave up leaves stale words, whose offsets could lie outside
+    // this call's weights: every entry then names expert 0 with weight 0 (the
+    // call's y is NaN in any case), so nothing below reads through them
+    if (__ballot(!got) == 0) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) ew[lane + j * 64] = v[j];
+      for (int j = 0; j < PER; ++j) ew[lane + j * 64] = v[j];
+    } else {
+      const uint32_t* e0 = reinterpret_cast<const uint32_t*>(a.experts);   // fmt, reserved, gate, up, down
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = lane + j * 64, f = i % kSelWords;
+        ew[i] = f == 0 ? e0[0] << 16 : f == 1 ? 0u : e0[f];
+      }
+    }
   }
   __syncthreads();
   if (tid() < n) {
@@ -1500,6 +1513,8 @@ int fused_workers() {
 // Tags of fused calls: unique in the process, so no word a workspace holds
 // from an earlier call can carry the tag of a later one.
 std::atomic<uint32_t> g_call_tag{0};
+std::atomic<int> g_spin_limit{dev::kSpinLimit};
+
 uint32_t next_tag() {
   uint32_t t;
   do t = g_call_tag.fetch_add(1, std::memory_order_relaxed) + 1; while (t == 0);
@@ -1516,6 +1531,7 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   if (workers <= 0) return MOE_EDEVICE;
   a.tag = next_tag();
   a.err = reinterpret_cast<uint32_t*>(w8 + l.err);
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.part_t = reinterpret_cast<uint64_t*>(w8 + l.part_t);
   a.lgt = reinterpret_cast<uint64_t*>(w8 + l.lgt);
   a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
@@ -1668,6 +1684,11 @@ const char* moe_status_string(int status) {
     case MOE_ECODE: return "invalid packed code";
     default: return "unknown status";
   }
+}
+
+int32_t moe_set_spin_limit(int32_t polls) {
+  if (polls < 0) return MOE_EINVAL;
+  return moe::g_spin_limit.exchange(polls, std::memory_order_relaxed);
 }
 
 int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll,

@@ -267,6 +267,20 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
                      int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Test aid: the fused launch's hand-off waits.                              */
+/* ------------------------------------------------------------------------ */
+
+/* Every wait of one moe_layer / moe_stack_decode launch on words published
+ * by another workgroup of the same launch gives up after `polls` polls
+ * (default 65536, tens of ms): the launch then still drains, the failure is
+ * recorded in the workspace's error word, the call's y is NaN, and a worker
+ * whose wait for the selection gave up computes with expert 0 instead of
+ * reading stale entries.  0 makes every wait give up at once, which lets a
+ * test reach that path without a hung producer.  Process-wide, read at each
+ * launch.  Returns the previous value, or MOE_EINVAL for polls < 0. */
+int32_t moe_set_spin_limit(int32_t polls);
+
+/* ------------------------------------------------------------------------ */
 /* Measurement aid (not a step of the method).                               */
 /* ------------------------------------------------------------------------ */
 

@@ -83,6 +83,37 @@ def test_tiny_deterministic_and_workspace_reuse():
     assert np.array_equal(ys[0], ys[3])            # bitwise reproducible
 
 
+def test_given_up_waits_give_nan_and_the_next_call_recovers():
+    """Failure path of the fused launch, forced from the host: with the spin
+    limit at 0 every hand-off wait gives up at once, yet the launch drains
+    and y is all NaN; the next call at the default limit, on the same
+    workspace, is bitwise the call before."""
+    wl = synth.WORKLOADS["tiny"]
+    dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
+    ws = LY.workspace(dl.dims, 4)
+    xd = G.device_inputs(wl, 0, synth.x_bf16(wl, 0, 4, 21))
+
+    def run():
+        idx = torch.zeros((4, 2), dtype=torch.int32, device="cuda")
+        wts = torch.zeros((4, 2), dtype=torch.float32, device="cuda")
+        y = torch.zeros((4, wl.hidden), dtype=torch.float32, device="cuda")
+        L.moe_layer(dl.dims, xd, 4, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
+                    idx, wts, y, ws)
+        torch.cuda.synchronize()
+        return y.cpu().numpy()
+
+    y_ok = run()
+    assert np.all(np.isfinite(y_ok))
+    prev = L.moe_set_spin_limit(0)
+    try:
+        y_fail = run()
+    finally:
+        L.moe_set_spin_limit(prev)
+    _say("NaN fraction with spin limit 0:", float(np.isnan(y_fail).mean()))
+    assert np.all(np.isnan(y_fail))
+    assert np.array_equal(run(), y_ok)
+
+
 def test_route_only_and_ffn_only_match_layer():
     wl = synth.WORKLOADS["tiny"]
     dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
