@@ -628,9 +628,8 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
       constexpr int PER = (I + kThreads - 1) / kThreads;
       for (int t = 0; t < nb; ++t) {
         const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
-        // first a sparse wait (one word in every I/kThreads, which samples
-        // every gate/up tile of 16 channels), then the whole vector once
-        (void)await_word(src + (tid() * (I / kThreads)), tag, a.err, a.spin_limit);
+        // the whole vector polled at once (a sparse first wait on one word
+        // per gate/up tile cost a round trip more than it saved in polls)
         uint32_t v[PER];
         await_batch<PER>(
             [src](int j) -> const uint64_t* {
