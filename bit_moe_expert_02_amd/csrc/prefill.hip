@@ -16,7 +16,7 @@
 //   count     rows per expert
 //   place     pairs (row, slot) grouped by expert, ascending pair index;
 //             chunks of at most kChunk pairs of one expert
-//   gateup    per (chunk, 128 channels): G = Xq W_gate^T, V = Xq W_up^T on the
+//   gateup    per (chunk, 256 channels): G = Xq W_gate^T, V = Xq W_up^T on the
 //             scaled matrix cores, h = silu(G) * V stored as f16
 //   down      per (chunk, 256 outputs): w * (h W_down^T) into per-pair partials
 //   combine   y[r] = the row's partials in ascending expert id
@@ -342,9 +342,8 @@ __device__ __forceinline__ void item_of_block(int b, int NT, int n_chunks, int& 
 // gate/up: work item (chunk, 256 channels); wave w of eight owns channels
 // c0 .. c0+31 of gate and up (four B fragments per K-step), every row tile of
 // the chunk.  The eight waves share one staged activation tile, so a chunk's
-// activations are read by I / 256 workgroups.
-// h = silu(G) * V is quantised to MXFP8 per (row, 32 channels) -- exactly the
-// wave's channels -- and stored at the pairs' expert-sorted positions.
+// activations are read by I / 256 workgroups.  h = silu(G) * V goes out as
+// f16 (round to nearest even) at the pairs' expert-sorted positions.
 template <int H, int I>
 __global__ __launch_bounds__(kGuThreads, 1) void k_gateup(Args a) {
   constexpr int NT = I / kGuCh, S = H / kStepK;
