@@ -171,3 +171,16 @@ def test_plan_offsets_and_sizes():
     for r in list(table) + list(shared):
         assert r["gate"] % 256 == 0 and r["up"] % 256 == 0 and r["down"] % 256 == 0
     assert total >= 9_953_280 + 7_624_704 + 15_206_400 + 37_601_280
+
+
+def test_spin_limit_setter(L):
+    """The hand-off spin limit is a process-wide host setting: the setter
+    returns the previous value and rejects a negative one (no device use)."""
+    lib = L.lib()
+    prev = lib.moe_set_spin_limit(1000)
+    try:
+        assert prev >= 0
+        assert lib.moe_set_spin_limit(-1) == -1          # MOE_EINVAL, limit unchanged
+        assert lib.moe_set_spin_limit(1000) == 1000
+    finally:
+        lib.moe_set_spin_limit(prev)
