@@ -1284,8 +1284,10 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   const int nsw = a.nsw < nsw_want ? a.nsw : nsw_want;
   if (w < nsw) {
     // shared gate/up tiles need only x: they stream while the selection is
-    // made.  They wait until the selection has every logit, so neither the
-    // router's loads nor the selection's poll queue behind this traffic.
+    // made.  At one row they wait until the selection has every logit, so
+    // neither the router's loads nor the selection's poll queue behind this
+    // traffic; with more rows the tiles are long enough that starting at
+    // once is worth more.
     if (tid() == 0) {
       sl.ref = shref;
       sl.expert = -1;
@@ -1295,7 +1297,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
         sl.pair[r] = a.R * a.k + r;
         sl.w[r] = 1.0f;
       }
-      (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err, a.spin_limit);
+      if (a.R == 1) (void)await_word(a.selt + (w % kSelRep) * kSelRepWords + kSelEntryWords, tag, a.err, a.spin_limit);
     }
     __syncthreads();
     for (int t = w; t < nsh; t += nsw) {
