@@ -14,7 +14,9 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
-MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EFORMAT, MOE_EWORKSPACE, MOE_EDEVICE, MOE_ECODE = 0, -1, -2, -3, -4, -5, -6
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EFORMAT, MOE_EWORKSPACE, MOE_EDEVICE, MOE_ECODE, MOE_ETIMEOUT = \
+    0, -1, -2, -3, -4, -5, -6, -7
+MOE_ACT_MXFP8 = 1
 FMT = {"TERN160": 1, "Q2_0": 2, "Q3": 3, "MXFP4": 4, "Q8": 5}
 FMT_NAME = {v: k for k, v in FMT.items()}
 MAX_DECODE_ROWS = 8
@@ -24,7 +26,7 @@ MAX_TOP_K = 8
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
            "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
-           "moe_stream_read", "moe_set_spin_limit")
+           "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status")
 
 
 class MoeError(RuntimeError):
@@ -35,7 +37,8 @@ class MoeError(RuntimeError):
 
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
 
 
 class LayerWeights(ctypes.Structure):
@@ -92,6 +95,8 @@ def lib():
         L.moe_set_spin_limit.argtypes = [i32]
         L.moe_stream_read.restype = ctypes.c_int
         L.moe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
+        L.moe_workspace_status.restype = ctypes.c_int
+        L.moe_workspace_status.argtypes = [vp, sz, vp]
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
@@ -143,8 +148,8 @@ def unpack(fmt, buf, n, k, nthreads=0):
 
 
 # ----------------------------------------------------------------------------- device calls
-def dims(hidden, inter, n_experts, top_k):
-    return Dims(hidden, inter, n_experts, top_k)
+def dims(hidden, inter, n_experts, top_k, flags=0):
+    return Dims(hidden, inter, n_experts, top_k, flags)
 
 
 def workspace_bytes(d, rows):
@@ -221,6 +226,15 @@ def moe_stream_read(buf, nbytes, sink, grid, unroll, stream=None):
     """Measurement aid: the streaming-read kernel over the first nbytes of buf."""
     _check("moe_stream_read", lib().moe_stream_read(_ptr(buf), int(nbytes), _ptr(sink), int(grid),
                                                     int(unroll), _stream(stream)))
+
+
+def moe_workspace_status(ws, stream=None):
+    """MOE_OK or MOE_ETIMEOUT (a fused call's hand-off wait gave up since the
+    last query); synchronises the stream and clears the workspace's error word."""
+    st = lib().moe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if st not in (MOE_OK, MOE_ETIMEOUT):
+        raise MoeError("moe_workspace_status", st)
+    return st
 
 
 def moe_set_spin_limit(polls):

@@ -15,8 +15,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["moe_kernels.hip", "prefill.hip", "pack.cpp"]
-HEADERS = ["dev_common.h", "formats_dev.h", "host_common.h", "prefill.h"]
+SOURCES = ["moe_kernels.hip", "prefill.hip", "pack.cpp", "host_api.cpp"]
+HEADERS = ["dev_common.h", "formats_dev.h", "host_api.h", "host_common.h", "layout.h", "prefill.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -35,59 +35,39 @@
 #include "../../include/moe.h"
 #include "dev_common.h"
 #include "formats_dev.h"
+#include "host_api.h"
 #include "host_common.h"
+#include "layout.h"
 #include "prefill.h"
 
 namespace moe {
 namespace dev {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = lay::kThreads;
 #ifndef MOE_WAVES_PER_EU
 #define MOE_WAVES_PER_EU 4  // occupancy floor: 4 waves per SIMD (<= 128 VGPRs)
 #endif
-constexpr int kMaxRows = MOE_MAX_DECODE_ROWS;  // rows per call on the decode path
-constexpr int kMaxK = MOE_MAX_TOP_K;
+constexpr int kMaxRows = lay::kMaxRows;        // rows per call on the decode path
+constexpr int kMaxK = lay::kMaxK;
 constexpr int kNTB = 1;                        // token rows staged in LDS at once
-constexpr int kMaxSlots = 64;                  // distinct routed experts per call (rows * top_k)
-constexpr int kNumFmt = 5;                     // format tags 1..5
+constexpr int kMaxSlots = lay::kMaxSlots;      // distinct routed experts per call (rows * top_k)
+constexpr int kNumFmt = lay::kNumFmt;          // format tags 1..5
 constexpr int kPrepWGs = 16;                   // workgroups building activation records
-constexpr int kSelQ = 8;                       // experts per lane in the selection (E <= 512)
-// A published selection entry of the fused launch, as tagged words: id | fmt << 16,
-// weight bits, then the gate, up and down offsets of the expert (low, high).
-constexpr int kSelWords = 8;
-// The fused launch publishes the selection in kSelRep copies, kSelRepWords
-// apart (separate lines and pages): the workers poll copy blockIdx % kSelRep,
-// so a thousand polling workgroups spread over many memory channels instead
-// of queueing on the same few lines.  Copy 0 is the one the combine reads.
-constexpr int kSelRep = 16;
-constexpr int kSelEntryWords = kMaxRows * kMaxK * kSelWords;
-// word kSelEntryWords of each copy: "the logits are all out" (payload 1),
-// published by the selection of row 0 as soon as its wait ends
-constexpr int kSelRepWords = kSelEntryWords + 64;
+constexpr int kSelQ = lay::kMaxExperts / 64;   // experts per lane in the selection
+// The published selection of the fused launch (layout.h): kSelWords tagged
+// words per entry in kSelRep copies, kSelRepWords apart.  The workers poll
+// copy blockIdx % kSelRep, so a thousand polling workgroups spread over many
+// memory channels instead of queueing on the same few lines.  Copy 0 is the
+// one the combine reads.  Word kSelEntryWords of each copy: "the logits are
+// all out" (payload 1), published by the selection of row 0 as soon as its
+// wait ends.
+constexpr int kSelWords = lay::kSelWords;
+constexpr int kSelRep = lay::kSelRep;
+constexpr int kSelEntryWords = lay::kSelEntryWords;
+constexpr int kSelRepWords = lay::kSelRepWords;
 
-// One entry of the slot table: a distinct selected expert (or the shared one)
-// and the rows it serves.
-struct SlotEntry {
-  moe_expert_ref ref;       // format and matrix offsets, copied from the expert table
-  int expert;               // routed id, -1 for the shared expert
-  int nt;                   // rows served
-  int row[kMaxRows];        // token row r
-  int pair[kMaxRows];       // h / partial row: r*k + kk (routed) or R*k + r (shared)
-  float w[kMaxRows];        // mixing weight (1 for the shared expert)
-};
-
-// The work of one call: slots [0, n_active) are the distinct routed experts in
-// ascending id, slot n_active the shared expert (when there is one).  Work
-// item i of the gate/up (down) launch is tile i - gu_off[s] of the slot s with
-// gu_off[s] <= i < gu_off[s + 1]; tile counts depend on each slot's format.
-struct SlotTable {
-  int n_active;             // distinct routed experts in this call
-  int n_slots;              // n_active, plus one for the shared expert
-  int n_gu, n_dn;           // work items of the gate/up and down launches
-  int gu_off[kMaxSlots + 2];
-  int dn_off[kMaxSlots + 2];
-  SlotEntry e[kMaxSlots + 1];
-};
+using lay::SlotEntry;
+using lay::SlotTable;
 
 struct Args {
   const uint16_t* x;              // [R x H] bf16
@@ -125,6 +105,15 @@ struct Args {
   int shared_early;               // 1: the shared expert's gate/up runs beside the router
                                   // (moe_layer), so the gate/up launch skips it
   int base_y;                     // fused launch: first combine workgroup
+  // many-row generic path: entries of at most kGenRows pairs of one expert
+  // run through the decode tiles (idx / wts are the given routing there)
+  lay::GenEntry* gen;             // [max_gen]
+  int32_t* gen_n;                 // [3]: entries, gate/up items, down items
+  int32_t* map_gu;                // gate/up item -> entry
+  int32_t* map_dn;                // down item -> entry
+  const int32_t* list;            // [R k]: pair ids grouped by expert, ascending
+  const int32_t* cnt;             // [E]: pairs per expert
+  int mfma;                       // 1: MXFP4 experts are left to the matrix cores
 };
 
 // ---------------------------------------------------------------------------
@@ -223,6 +212,14 @@ __device__ __forceinline__ int tiles_of(uint32_t fmt) {
     default: return 0;
   }
 }
+
+// the host sizes record rows and generic work maps with layout.h's copies of
+// these numbers
+static_assert(Shape<5120, 2304>::XROW == lay::max_rec_row(5120) && Shape<512, 256>::XROW == lay::max_rec_row(512),
+              "record row size");
+static_assert(Shape<5120, 2304>::MAX_TILES_GU == 576 && Shape<5120, 2304>::MAX_TILES_DN == 320 &&
+                  Shape<512, 256>::MAX_TILES_GU == 8 && Shape<512, 256>::MAX_TILES_DN == 8,
+              "generic-path tile counts in layout.h");
 
 // ---------------------------------------------------------------------------
 // activation records
@@ -621,22 +618,24 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
     const int nb = nt_all - t0 < kNTB ? nt_all - t0 : kNTB;
     if (Stream<F, I, LPR, NPG, C::G>::P > 1 || t0 == 0) st.load(0, mats, rows, H, valid);   // kept for later rows
     __syncthreads();
+    bool lost = false;   // a wait for h gave up: this tile's partials are NaN
     if constexpr (TAG) {
       // h comes from gate/up workgroups of the same launch: wait for its
       // tagged words and stage the values in LDS
       float* hs = reinterpret_cast<float*>(lds + S::LDS_BYTES);
       constexpr int PER = (I + kThreads - 1) / kThreads;
+      bool got = true;
       for (int t = 0; t < nb; ++t) {
         const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
         // the whole vector polled at once (a sparse first wait on one word
         // per gate/up tile cost a round trip more than it saved in polls)
         uint32_t v[PER];
-        await_batch<PER>(
-            [src](int j) -> const uint64_t* {
-              const int i = tid() + j * kThreads;
-              return i < I ? src + i : nullptr;
-            },
-            tag, a.err, v, a.spin_limit);
+        got = await_batch<PER>(
+                  [src](int j) -> const uint64_t* {
+                    const int i = tid() + j * kThreads;
+                    return i < I ? src + i : nullptr;
+                  },
+                  tag, a.err, v, a.spin_limit) && got;
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
           const int i = tid() + j * kThreads;
@@ -644,6 +643,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
         }
       }
       if (tid() < nb) srcs[tid()] = hs + tid() * I;
+      lost = __syncthreads_or(!got);
     } else {
       if (tid() < nb) srcs[tid()] = a.h + static_cast<size_t>(sl.pair[t0 + tid()]) * I;
     }
@@ -668,7 +668,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
 #pragma unroll
       for (int t = 0; t < kNTB; ++t) {
         if (t < nb) {
-          const float sc = inv_sigma[t] * sl.w[t0 + t];
+          const float sc = lost ? __builtin_nanf("") : inv_sigma[t] * sl.w[t0 + t];
 #pragma unroll
           for (int q = 0; q < NPG; ++q) {
             const size_t o = static_cast<size_t>(sl.pair[t0 + t]) * H + n0 + q;
@@ -891,7 +891,7 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
 // lowest id holding it (ballots), and retires that entry.
 __device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ],
                                            const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
-                                           const moe_expert_ref* refs);
+                                           const moe_expert_ref* refs, bool lost = false);
 
 // The lane's share of the selection-only bias (0 where there is none).
 __device__ __forceinline__ void load_bias(const Args& a, float (&bias)[kSelQ]) {
@@ -926,7 +926,7 @@ __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel
   float bias[kSelQ];   // loaded before the wait, off the critical path
   load_bias(a, bias);
   uint32_t half[2 * kSelQ];
-  await_batch<2 * kSelQ>(
+  const bool got = await_batch<2 * kSelQ>(
       [lg, lane, E = a.E](int j) -> const uint64_t* {
         const int e = lane + 64 * (j >> 1);
         return e < E ? lg + 2 * e + (j & 1) : nullptr;
@@ -937,12 +937,14 @@ __device__ __forceinline__ void select_row_tagged(const Args& a, int r, int* sel
 #pragma unroll
   for (int q = 0; q < kSelQ; ++q)
     lv[q] = __builtin_bit_cast(double, (static_cast<uint64_t>(half[2 * q + 1]) << 32) | half[2 * q]);
-  select_core(a, r, lv, bias, sel, wsel, tag, refs);
+  // a wait that gave up leaves stale halves: the ids still name real experts,
+  // but their weights are NaN, so nothing downstream looks valid
+  select_core(a, r, lv, bias, sel, wsel, tag, refs, __ballot(!got) != 0);
 }
 
 __device__ __forceinline__ void select_core(const Args& a, int r, const double (&lv)[kSelQ],
                                            const float (&bias)[kSelQ], int* sel, float* wsel, uint32_t tag,
-                                           const moe_expert_ref* refs) {
+                                           const moe_expert_ref* refs, bool lost) {
   const int lane = tid() & 63;
   // selection keys: the double key mapped to an unsigned 64-bit integer of
   // the same order (a NaN key of a real expert counts as -inf, -0 as +0),
@@ -1027,7 +1029,7 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
     const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(eb >> 32), j);
     s += __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
   }
-  const float w = static_cast<float>(e / s);
+  const float w = lost ? __builtin_nanf("") : static_cast<float>(e / s);
   if (lane < a.k) {
     sel[lane] = my_id;
     wsel[lane] = w;
@@ -1180,7 +1182,7 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
   const int r = i / S::kH, n = i - r * S::kH;
   const int k = a.k;
   uint32_t w[2 * kMaxK + 1];
-  await_batch<2 * kMaxK + 1>(
+  const bool got = await_batch<2 * kMaxK + 1>(
       [sel = a.selt, part = a.part_t, r, n, k, sh = a.shared != nullptr, R = a.R](int j) -> const uint64_t* {
         if (j < kMaxK) return j < k ? sel + kSelWords * (r * k + j) : nullptr;
         const int q = j - kMaxK;
@@ -1206,7 +1208,7 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
     if (pos < k) s += t;
   }
   if (a.shared) s += __builtin_bit_cast(float, w[2 * kMaxK]);
-  if (__hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
+  if (!got || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
   a.y[i] = s;
   if (a.x_next) {   // stack decode: x_{l+1} = bf16 (round to nearest even) of the fp32 y + noise
     const float v = a.noise ? s + a.noise[i] : s;
@@ -1327,8 +1329,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
         },
         tag, a.err, v, a.spin_limit);
     // a wait that gave up leaves stale words, whose offsets could lie outside
-    // this call's weights: every entry then names expert 0 with weight 0 (the
-    // call's y is NaN in any case), so nothing below reads through them
+    // this call's weights: every entry then names expert 0 with weight NaN,
+    // so nothing below reads through them and every partial it makes is NaN
     if (__ballot(!got) == 0) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) ew[lane + j * 64] = v[j];
@@ -1337,7 +1339,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
         const int i = lane + j * 64, f = i % kSelWords;
-        ew[i] = f == 0 ? e0[0] << 16 : f == 1 ? 0u : e0[f];
+        ew[i] = f == 0 ? e0[0] << 16 : f == 1 ? 0x7FC00000u : e0[f];
       }
     }
   }
@@ -1391,6 +1393,132 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   a.y[i] = s;
 }
 
+// ---------------------------------------------------------------------------
+// many-row generic path: the decode tiles over entries of at most kGenRows
+// pairs of one expert (any format, and the shared expert), h in fp32
+// ---------------------------------------------------------------------------
+// Exclusive prefix sum of v over the workgroup's threads in thread order;
+// *total gets the sum of all.  tmp: kThreads ints of LDS.
+__device__ __forceinline__ int wg_scan(int v, int* tmp, int* total) {
+  const int t = tid();
+  tmp[t] = v;
+  __syncthreads();
+  for (int o = 1; o < kThreads; o <<= 1) {
+    const int add = t >= o ? tmp[t - o] : 0;
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const int incl = tmp[t];
+  *total = tmp[kThreads - 1];
+  __syncthreads();
+  return incl - v;
+}
+
+// Plan (one workgroup): the generic entries of every routed expert in
+// ascending id (those the matrix cores do not take), each with the offsets of
+// its first gate/up and down items, then the shared expert's entries; counts
+// in gen_n.  Thread t handles experts 2t and 2t + 1 (E <= 2 * kThreads).
+template <class S>
+__global__ __launch_bounds__(kThreads) void k_gen_plan(Args a) {
+  static_assert(lay::kMaxExperts <= 2 * kThreads, "two experts per thread");
+  __shared__ int tmp[kThreads];
+  constexpr int G = lay::kGenRows;
+  const int t = tid();
+  int c[2], n[2], tg[2], td[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int e = 2 * t + j;
+    c[j] = e < a.E ? a.cnt[e] : 0;
+    const uint32_t fmt = e < a.E ? a.experts[e].fmt : 0u;
+    const bool gen = c[j] > 0 && !(a.mfma && fmt == MOE_FMT_MXFP4);
+    n[j] = gen ? (c[j] + G - 1) / G : 0;
+    tg[j] = tiles_of<S, true>(fmt);
+    td[j] = tiles_of<S, false>(fmt);
+  }
+  int tot_c, tot_n, tot_g, tot_d;
+  const int off_c = wg_scan(c[0] + c[1], tmp, &tot_c);
+  const int off_n = wg_scan(n[0] + n[1], tmp, &tot_n);
+  const int off_g = wg_scan(n[0] * tg[0] + n[1] * tg[1], tmp, &tot_g);
+  const int off_d = wg_scan(n[0] * td[0] + n[1] * td[1], tmp, &tot_d);
+  int oc = off_c, on = off_n, og = off_g, od = off_d;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    for (int q = 0; q < n[j]; ++q) {
+      const int m = c[j] - G * q < G ? c[j] - G * q : G;
+      a.gen[on + q] = lay::GenEntry{2 * t + j, oc + G * q, m, og + q * tg[j], od + q * td[j]};
+    }
+    oc += c[j];
+    on += n[j];
+    og += n[j] * tg[j];
+    od += n[j] * td[j];
+  }
+  // the shared expert: every row, in entries of G rows
+  const int nsh = a.shared ? (a.R + G - 1) / G : 0;
+  const uint32_t sfmt = a.shared ? a.shared->fmt : 0u;
+  const int sg = tiles_of<S, true>(sfmt), sd = tiles_of<S, false>(sfmt);
+  for (int q = t; q < nsh; q += kThreads) {
+    const int m = a.R - G * q < G ? a.R - G * q : G;
+    a.gen[tot_n + q] = lay::GenEntry{-1, G * q, m, tot_g + q * sg, tot_d + q * sd};
+  }
+  if (t == 0) {
+    a.gen_n[0] = tot_n + nsh;
+    a.gen_n[1] = tot_g + nsh * sg;
+    a.gen_n[2] = tot_d + nsh * sd;
+  }
+}
+
+// Item maps: workgroup i writes entry i's gate/up and down items.
+template <class S>
+__global__ __launch_bounds__(kThreads) void k_gen_fill(Args a) {
+  const int i = blockIdx.x;
+  if (i >= a.gen_n[0]) return;
+  const lay::GenEntry ge = a.gen[i];
+  const uint32_t fmt = ge.expert >= 0 ? a.experts[ge.expert].fmt : a.shared->fmt;
+  const int tg = tiles_of<S, true>(fmt), td = tiles_of<S, false>(fmt);
+  for (int q = tid(); q < tg; q += kThreads) a.map_gu[ge.gu_off + q] = i;
+  for (int q = tid(); q < td; q += kThreads) a.map_dn[ge.dn_off + q] = i;
+}
+
+// Gate/up (GU) or down items of the generic entries, grid-striding.  A routed
+// entry's pairs come from the expert-sorted list (row = pair / k, weight =
+// the routing weight); the shared expert's pairs are R*k + r with weight 1.
+template <class S, bool GU>
+__global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_gen_ffn(Args a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ SlotEntry sl;
+  __shared__ int tile_s;
+  const int n_items = uniform(a.gen_n[GU ? 1 : 2]);
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    if (tid() < lay::kGenRows) {
+      const int i = (GU ? a.map_gu : a.map_dn)[item];
+      const lay::GenEntry ge = a.gen[i];
+      const int t = tid();
+      if (t == 0) {
+        sl.ref = ge.expert >= 0 ? a.experts[ge.expert] : *a.shared;
+        sl.expert = ge.expert;
+        sl.nt = ge.m;
+        tile_s = item - (GU ? ge.gu_off : ge.dn_off);
+      }
+      if (t < ge.m) {
+        if (ge.expert >= 0) {
+          const int pair = a.list[ge.s0 + t];
+          sl.row[t] = pair / a.k;
+          sl.pair[t] = pair;
+          sl.w[t] = a.wts[pair];
+        } else {
+          sl.row[t] = ge.s0 + t;
+          sl.pair[t] = a.R * a.k + ge.s0 + t;
+          sl.w[t] = 1.0f;
+        }
+      }
+    }
+    __syncthreads();
+    run_slot<S, GU ? 2 : 0, false>(a, sl, uniform(tile_s), lds);
+    __syncthreads();
+  }
+}
+
 // Streaming-read ceiling: every lane reads U 16-byte chunks per iteration,
 // grid-striding, and folds them into an xor checksum.
 template <int U>
@@ -1421,58 +1549,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4* __restric
 // ===========================================================================
 namespace {
 
-struct WsLayout {
-  size_t err, logits, idx, wts, slots, order, xinv, xrec, h, part, lgt, selt, ht, part_t, total;
-  int xrow;
-};
-
-size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
-int xrow_for(const moe_dims& d) {
-  if (d.hidden == 5120) return dev::Shape<5120, 2304>::XROW;
-  return dev::Shape<512, 256>::XROW;
-}
-
-WsLayout ws_layout(const moe_dims& d, int rows) {
-  WsLayout l{};
-  size_t o = 0;
-  const size_t pairs = static_cast<size_t>(rows) * d.top_k + rows;
-  l.xrow = xrow_for(d);
-  l.err = o;      o = align_up(o + 16, 256);
-  l.logits = o;   o = align_up(o + 8 * static_cast<size_t>(rows) * d.n_experts, 256);
-  l.idx = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
-  l.wts = o;      o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
-  l.slots = o;    o = align_up(o + sizeof(dev::SlotTable), 256);
-  l.order = o;    o = align_up(o + 4 * static_cast<size_t>(rows) * d.top_k, 256);
-  l.xinv = o;     o = align_up(o + 4 * static_cast<size_t>(dev::kNumFmt) * rows, 256);
-  l.xrec = o;     o = align_up(o + static_cast<size_t>(dev::kNumFmt) * rows * l.xrow, 256);
-  l.h = o;        o = align_up(o + 4 * pairs * d.inter, 256);
-  l.part = o;     o = align_up(o + 4 * pairs * d.hidden, 256);
-  l.lgt = o;      o = align_up(o + 16 * static_cast<size_t>(rows) * d.n_experts, 256);
-  l.selt = o;     o = align_up(o + 8 * static_cast<size_t>(dev::kSelRep) * dev::kSelRepWords, 256);
-  l.ht = o;       o = align_up(o + 8 * pairs * d.inter, 256);
-  l.part_t = o;   o = align_up(o + 8 * pairs * d.hidden, 256);
-  l.total = o;
-  return l;
-}
-
-int shape_class(const moe_dims* d) {
-  if (d->hidden == 5120 && d->inter == 2304) return 1;
-  if (d->hidden == 512 && d->inter == 256) return 2;
-  return 0;
-}
-
-int check_dims(const moe_dims* d, int rows) {
-  if (!d) return MOE_EINVAL;
-  if (rows < 0) return MOE_EINVAL;
-  if (!shape_class(d)) return MOE_ESHAPE;
-  if (d->top_k < 1 || d->top_k > MOE_MAX_TOP_K || d->n_experts < d->top_k ||
-      d->n_experts > 64 * dev::kSelQ)
-    return MOE_ESHAPE;
-  if (rows > MOE_MAX_DECODE_ROWS || rows * d->top_k > 64) return MOE_ESHAPE;
-  return MOE_OK;
-}
-
+int shape_class(const moe_dims* d) { return lay::shape_class(*d); }
 
 // Grid of a work-list launch: enough workgroups for every item of the
 // heaviest format mix, capped (items beyond the grid are strided over).
@@ -1524,7 +1601,7 @@ uint32_t next_tag() {
 
 // moe_layer: one fused launch.
 template <class S>
-int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const WsLayout& l,
+int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const lay::TaggedLayout& l,
                  hipStream_t s, void* const* events, int n_events) {
   const int n_routed = rows * d->top_k;
   const bool sh = a.shared != nullptr;
@@ -1554,14 +1631,6 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const Ws
   hipLaunchKernelGGL(dev::k_layer<S>, dim3(a.base_y + ny), dim3(dev::kThreads), lds, s, a);
   rec();
   if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
-  return MOE_OK;
-}
-
-int check_prefill_dims(const moe_dims* d, int rows) {
-  if (!d) return MOE_EINVAL;
-  if (!shape_class(d)) return MOE_ESHAPE;
-  if (d->top_k < 1 || d->top_k > MOE_MAX_TOP_K || d->n_experts < d->top_k) return MOE_ESHAPE;
-  if (rows > MOE_MAX_PREFILL_ROWS) return MOE_ESHAPE;
   return MOE_OK;
 }
 
@@ -1625,7 +1694,7 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   if (route && !w_router) return MOE_EINVAL;
   if (ffn && (!weights || !experts || !y)) return MOE_EINVAL;
   if (!route && (!idx || !wts)) return MOE_EINVAL;
-  const WsLayout l = ws_layout(*d, rows);
+  const lay::DecodeLayout l = lay::decode_layout(*d, rows);
   if (ws_bytes < l.total) return MOE_EWORKSPACE;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   dev::Args a{};
@@ -1657,8 +1726,8 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (route && ffn) {
     switch (shape_class(d)) {
-      case 1: return launch_fused<dev::Shape<5120, 2304>>(d, rows, a, w8, l, s, events, n_events);
-      case 2: return launch_fused<dev::Shape<512, 256>>(d, rows, a, w8, l, s, events, n_events);
+      case 1: return launch_fused<dev::Shape<5120, 2304>>(d, rows, a, w8, lay::tagged_layout(*d), s, events, n_events);
+      case 2: return launch_fused<dev::Shape<512, 256>>(d, rows, a, w8, lay::tagged_layout(*d), s, events, n_events);
       default: return MOE_ESHAPE;
     }
   }
@@ -1669,22 +1738,63 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   }
 }
 
+template <class S>
+int launch_generic(const gen::Launch& g, hipStream_t s) {
+  dev::Args a{};
+  a.x = static_cast<const uint16_t*>(g.x);
+  a.idx = const_cast<int32_t*>(g.idx);
+  a.wts = const_cast<float*>(g.wts);
+  a.weights = static_cast<const uint8_t*>(g.weights);
+  a.experts = g.experts;
+  a.shared = g.shared;
+  a.h = g.h32;
+  a.part = g.part;
+  a.gen = g.gen;
+  a.gen_n = g.gen_n;
+  a.map_gu = g.map_gu;
+  a.map_dn = g.map_dn;
+  a.list = g.list;
+  a.cnt = g.cnt;
+  a.mfma = g.mfma;
+  a.R = g.rows;
+  a.k = g.top_k;
+  a.E = g.n_experts;
+  hipLaunchKernelGGL(dev::k_gen_plan<S>, dim3(1), dim3(dev::kThreads), 0, s, a);
+  hipLaunchKernelGGL(dev::k_gen_fill<S>, dim3(g.max_gen), dim3(dev::kThreads), 0, s, a);
+  hipLaunchKernelGGL((dev::k_gen_ffn<S, true>), dim3(item_grid(g.max_items_gu)), dim3(dev::kThreads),
+                     S::LDS_WITH_STAGE, s, a);
+  hipLaunchKernelGGL((dev::k_gen_ffn<S, false>), dim3(item_grid(g.max_items_dn)), dim3(dev::kThreads),
+                     S::LDS_WITH_STAGE, s, a);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}
+
 }  // namespace
+
+namespace gen {
+int launch(const moe_dims* d, const Launch& g, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (shape_class(d)) {
+    case 1: return launch_generic<dev::Shape<5120, 2304>>(g, s);
+    case 2: return launch_generic<dev::Shape<512, 256>>(g, s);
+    default: return MOE_ESHAPE;
+  }
+}
+}  // namespace gen
 }  // namespace moe
 
 extern "C" {
 
-const char* moe_status_string(int status) {
-  switch (status) {
-    case MOE_OK: return "ok";
-    case MOE_EINVAL: return "invalid argument";
-    case MOE_ESHAPE: return "unsupported shape";
-    case MOE_EFORMAT: return "unknown weight format";
-    case MOE_EWORKSPACE: return "workspace too small";
-    case MOE_EDEVICE: return "HIP launch or runtime error";
-    case MOE_ECODE: return "invalid packed code";
-    default: return "unknown status";
-  }
+int moe_workspace_status(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < 16) return MOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint32_t err = 0;
+  // the error word is the first word of every workspace (layout.h)
+  if (hipMemcpyAsync(&err, ws, sizeof(err), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_EDEVICE;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_EDEVICE;
+  if (err == 0) return MOE_OK;
+  if (hipMemsetAsync(ws, 0, sizeof(err), s) != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+    return MOE_EDEVICE;
+  return MOE_ETIMEOUT;
 }
 
 int32_t moe_set_spin_limit(int32_t polls) {
@@ -1710,39 +1820,9 @@ int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 
-size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows) {
-  if (rows > MOE_MAX_DECODE_ROWS) {
-    if (moe::check_prefill_dims(dims, rows)) return 0;
-    return moe::pf::workspace_bytes(*dims, rows);
-  }
-  if (moe::check_dims(dims, rows < 1 ? 1 : rows)) return 0;
-  return moe::ws_layout(*dims, rows < 1 ? 1 : rows).total;
-}
-
 int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, void* scales,
                     void* stream) {
   return moe::pf::quant(x_bf16, rows, k, codes, scales, stream);
-}
-
-int moe_check_experts(const moe_dims* dims, const moe_expert_ref* table, int32_t count,
-                      size_t weights_bytes) {
-  if (!dims || !table || count < 0) return MOE_EINVAL;
-  if (!moe::shape_class(dims)) return MOE_ESHAPE;
-  for (int i = 0; i < count; ++i) {
-    const moe_expert_ref& r = table[i];
-    if (moe::format_info(static_cast<int>(r.fmt)).block == 0) return MOE_EFORMAT;
-    if (r.reserved != 0) return MOE_EINVAL;
-    const size_t gu = moe::packed_bytes(static_cast<int>(r.fmt), dims->inter, dims->hidden);
-    const size_t dn = moe::packed_bytes(static_cast<int>(r.fmt), dims->hidden, dims->inter);
-    if (!gu || !dn) return MOE_ESHAPE;
-    const uint64_t offs[3] = {r.gate, r.up, r.down};
-    const size_t sizes[3] = {gu, gu, dn};
-    for (int m = 0; m < 3; ++m) {
-      if (offs[m] % 16) return MOE_EINVAL;
-      if (offs[m] > weights_bytes || sizes[m] > weights_bytes - offs[m]) return MOE_EINVAL;
-    }
-  }
-  return MOE_OK;
 }
 
 int moe_route(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
@@ -1758,7 +1838,7 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
                    void* stream) {
   if (rows > MOE_MAX_DECODE_ROWS) {
-    if (int st = moe::check_prefill_dims(dims, rows)) return st;
+    if (int st = moe::check_many_row_dims(dims, rows)) return st;
     return moe::pf::run(dims, x_bf16, rows, idx, wts, weights, experts, shared, y, ws, ws_bytes,
                         stream);
   }

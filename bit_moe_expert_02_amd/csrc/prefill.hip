@@ -1,5 +1,7 @@
-// gfx950 prefill path of the routed-MoE expert FFN: many rows per call
-// (a prompt, thousands of tokens), every selected expert in MXFP4.
+// gfx950 many-row (prefill) path of the routed-MoE expert FFN: many rows per
+// call (a prompt, thousands of tokens).  MXFP4 experts run here on the
+// matrix cores; every other expert, and the shared expert, runs the decode
+// tiles on the same expert-grouped pair lists (moe_kernels.hip).
 //
 // The experts become a grouped, dense contraction here -- each selected
 // expert sees tens to hundreds of rows -- so the products run on the scaled
@@ -48,7 +50,7 @@ using dev::bload64;
 using dev::uniform;
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 64;               // pairs of one expert per work item
+constexpr int kChunk = lay::kChunk;      // pairs of one expert per work item
 constexpr int kRowTiles = kChunk / 16;   // 16-row matrix-core tiles per chunk
 constexpr int kStepK = 128;              // K per matrix-core instruction
 // LDS row pitch of the staged activation tiles: one 16-byte slot more than a
@@ -66,11 +68,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-struct Chunk {
-  int expert;   // routed id
-  int s0;       // first position in the expert-sorted pair list
-  int m;        // pairs in this chunk (1 .. kChunk)
-};
+using lay::Chunk;
 
 struct Args {
   const uint16_t* x;              // [R x H] bf16
@@ -86,8 +84,10 @@ struct Args {
   Chunk* chunks;                  // [max_chunks]
   int32_t* n_chunks;              // [1]
   uint16_t* hq;                   // [R k x I] f16 h, expert-sorted positions
-  float* part;                    // [R k x H] per-pair partial outputs (pair id order)
+  float* part;                    // [(R k + R) x H] per-pair partial outputs (pair id
+                                  // order; the shared expert's rows last)
   int R, k, E, H, I;
+  int has_shared;                 // the combine adds the shared expert's partials
 };
 
 // ---------------------------------------------------------------------------
@@ -357,14 +357,14 @@ __global__ __launch_bounds__(kGuThreads, 1) void k_gateup(Args a) {
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
   const moe_expert_ref ref = a.experts[uniform(ch.expert)];
-  const bool ok = uniform(static_cast<int>(ref.fmt)) == MOE_FMT_MXFP4;
+  if (uniform(static_cast<int>(ref.fmt)) != MOE_FMT_MXFP4) return;   // a generic entry's pairs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
   if (threadIdx.x < kChunk) src[threadIdx.x] = threadIdx.x < m ? a.list[s0 + threadIdx.x] / a.k : -1;
   __syncthreads();
   const int mt = (m + 15) / 16;
   const uint32_t mbytes = static_cast<uint32_t>(I) * (H / 32) * 17u;
-  const Buf mg = make_buf(a.weights + ref.gate, ok ? mbytes : 0u);
-  const Buf mu = make_buf(a.weights + ref.up, ok ? mbytes : 0u);
+  const Buf mg = make_buf(a.weights + ref.gate, mbytes);
+  const Buf mu = make_buf(a.weights + ref.up, mbytes);
   const Buf xb = make_buf(a.xq, static_cast<uint32_t>(a.R) * H);
   const Buf xsb = make_buf(a.xs, static_cast<uint32_t>(a.R) * (H / 32));
   const int c0 = nt * kGuCh + wave * 32;
@@ -454,9 +454,8 @@ __global__ __launch_bounds__(kGuThreads, 1) void k_gateup(Args a) {
       for (int r = 0; r < 4; ++r) {
         const int row = rt * 16 + 4 * g + r;
         const float g0 = acc[rt][0][r], g1 = acc[rt][1][r];
-        float h0 = g0 / (1.0f + __expf(-g0)) * acc[rt][2][r];
-        float h1 = g1 / (1.0f + __expf(-g1)) * acc[rt][3][r];
-        if (!ok) h0 = h1 = __builtin_nanf("");      // the expert is not MXFP4
+        const float h0 = g0 / (1.0f + __expf(-g0)) * acc[rt][2][r];
+        const float h1 = g1 / (1.0f + __expf(-g1)) * acc[rt][3][r];
         if (row < m) {
           uint16_t* hrow = a.hq + static_cast<size_t>(s0 + row) * I;
           hrow[c0 + j] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(h0));
@@ -483,13 +482,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   const Chunk ch = a.chunks[ci];
   const int m = uniform(ch.m), s0 = uniform(ch.s0);
   const moe_expert_ref ref = a.experts[uniform(ch.expert)];
-  const bool ok = uniform(static_cast<int>(ref.fmt)) == MOE_FMT_MXFP4;
+  if (uniform(static_cast<int>(ref.fmt)) != MOE_FMT_MXFP4) return;   // a generic entry's pairs
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15, g = lane >> 4;
   if (threadIdx.x < kChunk) src[threadIdx.x] = threadIdx.x < m ? s0 + threadIdx.x : -1;
   __syncthreads();
   const int mt = (m + 15) / 16;
   const uint32_t mbytes = static_cast<uint32_t>(H) * (I / 32) * 17u;
-  const Buf md = make_buf(a.weights + ref.down, ok ? mbytes : 0u);
+  const Buf md = make_buf(a.weights + ref.down, mbytes);
   const Buf hb = make_buf(reinterpret_cast<const uint8_t*>(a.hq), static_cast<uint32_t>(a.R * a.k) * I * 2u);
   const int c0 = nt * kDnCh + wave * 64;
   // h tile loader: kChunk rows x 128 f16 = 16 KB, four 16-byte chunks per thread
@@ -600,7 +599,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
         const int row = rt * 16 + 4 * g + r;
         if (row < m) {
           const int pair = a.list[s0 + row];
-          const float w = ok ? a.wts[pair] : __builtin_nanf("");
+          const float w = a.wts[pair];
           float* out = a.part + static_cast<size_t>(pair) * H + c0 + j;
 #pragma unroll
           for (int f = 0; f < 4; ++f) out[16 * f] = acc[rt][f][r] * w;
@@ -610,8 +609,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_down(Args a) {
   }
 }
 
-// y[r] = the row's k partials in ascending expert id (a fixed order, so y is
-// bitwise reproducible); an id outside [0, E) yields NaN.
+// y[r] = the row's k partials in ascending expert id, then the shared
+// expert's (a fixed order, so y is bitwise reproducible); an id outside
+// [0, E) yields NaN.
 template <int H>
 __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   const int i = blockIdx.x * kThreads + threadIdx.x;
@@ -640,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
     for (int q = 0; q < MOE_MAX_TOP_K; ++q) t = rank[q] == pos ? v[q] : t;
     if (pos < a.k) s += t;
   }
+  if (a.has_shared) s += a.part[static_cast<size_t>(a.R * a.k + r) * H + n];
   a.y[i] = bad ? __builtin_nanf("") : s;
 }
 
@@ -650,41 +651,25 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
 // ===========================================================================
 namespace {
 
-size_t al(size_t v) { return (v + 255) / 256 * 256; }
-
-struct PfLayout {
-  size_t xq, xs, cnt, list, chunks, n_chunks, hq, part, total;
-  int max_chunks;
-};
-
-PfLayout pf_layout(const moe_dims& d, int rows) {
-  PfLayout l{};
-  const size_t R = rows, P = static_cast<size_t>(rows) * d.top_k, H = d.hidden, I = d.inter;
-  l.max_chunks = static_cast<int>((P + pf::kChunk - 1) / pf::kChunk) + d.n_experts;
-  size_t o = 0;
-  l.xq = o;       o = al(o + R * H);
-  l.xs = o;       o = al(o + R * H / 32);
-  l.cnt = o;      o = al(o + 4 * static_cast<size_t>(d.n_experts));
-  l.list = o;     o = al(o + 4 * P);
-  l.chunks = o;   o = al(o + sizeof(pf::Chunk) * static_cast<size_t>(l.max_chunks));
-  l.n_chunks = o; o = al(o + 4);
-  l.hq = o;       o = al(o + 2 * P * I);
-  l.part = o;     o = al(o + 4 * P * H);
-  l.total = o;
-  return l;
-}
-
 template <int H, int I>
-int launch_prefill(const moe_dims* d, int rows, pf::Args a, const PfLayout& l, hipStream_t s) {
-  const int nb = (rows * (H / 32) + pf::kThreads - 1) / pf::kThreads;
-  hipLaunchKernelGGL(pf::k_quant, dim3(nb), dim3(pf::kThreads), 0, s, a.x, rows, H, a.xq, a.xs);
+int launch_prefill(const moe_dims* d, int rows, pf::Args a, const lay::ManyRowLayout& l, const gen::Launch& g,
+                   hipStream_t s) {
+  const bool mfma = (d->flags & MOE_ACT_MXFP8) != 0;
+  if (mfma) {
+    const int nb = (rows * (H / 32) + pf::kThreads - 1) / pf::kThreads;
+    hipLaunchKernelGGL(pf::k_quant, dim3(nb), dim3(pf::kThreads), 0, s, a.x, rows, H, a.xq, a.xs);
+  }
   hipLaunchKernelGGL(pf::k_count, dim3(d->n_experts), dim3(pf::kThreads), 0, s, a);
   hipLaunchKernelGGL(pf::k_place, dim3(d->n_experts), dim3(pf::kThreads), 0, s, a);
-  const int chunk_groups = (l.max_chunks + pf::kXcd - 1) / pf::kXcd;   // ids cover every chunk slot
-  hipLaunchKernelGGL((pf::k_gateup<H, I>), dim3(chunk_groups * pf::kXcd * (I / pf::kGuCh)), dim3(pf::kGuThreads), 0,
-                     s, a);
-  hipLaunchKernelGGL((pf::k_down<H, I>), dim3(chunk_groups * pf::kXcd * (H / pf::kDnCh)), dim3(pf::kThreads), 0, s,
-                     a);
+  if (hipGetLastError() != hipSuccess) return MOE_EDEVICE;
+  if (int st = gen::launch(d, g, s)) return st;
+  if (mfma) {
+    const int chunk_groups = (l.max_chunks + pf::kXcd - 1) / pf::kXcd;   // ids cover every chunk slot
+    hipLaunchKernelGGL((pf::k_gateup<H, I>), dim3(chunk_groups * pf::kXcd * (I / pf::kGuCh)),
+                       dim3(pf::kGuThreads), 0, s, a);
+    hipLaunchKernelGGL((pf::k_down<H, I>), dim3(chunk_groups * pf::kXcd * (H / pf::kDnCh)),
+                       dim3(pf::kThreads), 0, s, a);
+  }
   hipLaunchKernelGGL(pf::k_combine<H>, dim3((rows * H + pf::kThreads - 1) / pf::kThreads),
                      dim3(pf::kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
@@ -694,14 +679,11 @@ int launch_prefill(const moe_dims* d, int rows, pf::Args a, const PfLayout& l, h
 
 namespace pf {
 
-size_t workspace_bytes(const moe_dims& d, int rows) { return pf_layout(d, rows).total; }
-
 int run(const moe_dims* d, const void* x, int rows, const int32_t* idx, const float* wts,
         const void* weights, const moe_expert_ref* experts, const moe_expert_ref* shared, float* y,
         void* ws, size_t ws_bytes, void* stream) {
   if (!x || !idx || !wts || !weights || !experts || !y || !ws) return MOE_EINVAL;
-  if (shared) return MOE_ESHAPE;   // the prefill path serves routed experts only
-  const PfLayout l = pf_layout(*d, rows);
+  const lay::ManyRowLayout l = lay::many_row_layout(*d, rows);
   if (ws_bytes < l.total) return MOE_EWORKSPACE;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   Args a{};
@@ -724,9 +706,32 @@ int run(const moe_dims* d, const void* x, int rows, const int32_t* idx, const fl
   a.E = d->n_experts;
   a.H = d->hidden;
   a.I = d->inter;
+  a.has_shared = shared != nullptr;
+  gen::Launch g{};
+  g.x = x;
+  g.idx = idx;
+  g.wts = wts;
+  g.weights = weights;
+  g.experts = experts;
+  g.shared = shared;
+  g.cnt = a.cnt;
+  g.list = a.list;
+  g.gen = reinterpret_cast<lay::GenEntry*>(w8 + l.gen);
+  g.gen_n = reinterpret_cast<int32_t*>(w8 + l.n_gen);
+  g.map_gu = reinterpret_cast<int32_t*>(w8 + l.map_gu);
+  g.map_dn = reinterpret_cast<int32_t*>(w8 + l.map_dn);
+  g.h32 = reinterpret_cast<float*>(w8 + l.h32);
+  g.part = a.part;
+  g.rows = rows;
+  g.top_k = d->top_k;
+  g.n_experts = d->n_experts;
+  g.mfma = (d->flags & MOE_ACT_MXFP8) ? 1 : 0;
+  g.max_gen = l.max_gen;
+  g.max_items_gu = l.max_items_gu;
+  g.max_items_dn = l.max_items_dn;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d->hidden == 5120 && d->inter == 2304) return launch_prefill<5120, 2304>(d, rows, a, l, s);
-  if (d->hidden == 512 && d->inter == 256) return launch_prefill<512, 256>(d, rows, a, l, s);
+  if (d->hidden == 5120 && d->inter == 2304) return launch_prefill<5120, 2304>(d, rows, a, l, g, s);
+  if (d->hidden == 512 && d->inter == 256) return launch_prefill<512, 256>(d, rows, a, l, g, s);
   return MOE_ESHAPE;
 }
 

@@ -52,10 +52,10 @@ class DeviceLayer:
     uint8 arrays; slot e takes pool[fmt][e % len(pool[fmt])].
     """
 
-    def __init__(self, wl, layer, materialize=(), pool=None, device="cuda"):
+    def __init__(self, wl, layer, materialize=(), pool=None, device="cuda", packed=None, flags=0):
         import torch
         self.wl, self.layer = wl, layer
-        self.dims = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k)
+        self.dims = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k, flags)
         self.fmts = synth.format_map(wl, layer)
         table, shared, total = plan(self.fmts, wl.shared_fmt, wl.hidden, wl.inter)
         self.table, self.shared_table, self.total = table, shared, total
@@ -71,6 +71,14 @@ class DeviceLayer:
             self._put(e, *self.pack_expert(e))
             self.materialized.add(e)
             self.source[e] = (layer, e)
+        # experts this layer's own weights were already packed for (e ->
+        # (gate, up, down) bytes from moe_pack of synth.expert_weights(wl, layer, e))
+        for e, trip in sorted((packed or {}).items()):
+            if e == wl.n_experts:
+                continue                     # the shared expert is packed below
+            self._put(int(e), *trip)
+            self.materialized.add(int(e))
+            self.source[int(e)] = (layer, int(e))
         if pool is not None:
             for e in range(wl.n_experts):
                 if e not in self.materialized:
@@ -78,7 +86,8 @@ class DeviceLayer:
                     self._put_dev(e, p[e % len(p)])
                     self.source[e] = (pool_layer(layer_of_pool(pool), self.fmts[e]), e % len(p))
         if wl.shared_fmt is not None:
-            self._put(-1, *self.pack_expert(wl.n_experts))
+            sh = (packed or {}).get(wl.n_experts)
+            self._put(-1, *(sh if sh is not None else self.pack_expert(wl.n_experts)))
         self.experts = torch.from_numpy(table.view(np.uint8).copy()).to(device)
         self.shared = (torch.from_numpy(shared.view(np.uint8).copy()).to(device)
                        if shared is not None else None)

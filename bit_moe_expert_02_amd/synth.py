@@ -11,7 +11,9 @@ Distributions (the pages have no real weights to offer; these stand in):
   x            fp32 N(0, 1) rounded to bf16 (round to nearest even)
   router       fp32 N(0, 0.02^2)        [E x H]
   experts      fp32 N(0, 0.02^2)        gate, up [I x H]; down [H x I]
-  bias         fp32 U(-0.6, 1.0)        one per expert (selection only)
+  bias         fp32 U(-0.6, 1.0)        one per expert (selection only), or the
+               residency policy: +1.0 / 0 / -0.6 by tier, times a scale
+  correlated   rows of a verify window x_r = rho x_0 + sqrt(1 - rho^2) z_r
   format map   exact per-layer counts from the shares 42.8 / 39.2 / 18.0 %
                (ternary / Q2_0 / Q3, [P3 §五.1]) placed by a seeded permutation
 """
@@ -21,11 +23,13 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # tensor ids in the spawn key
-T_X, T_ROUTER, T_BIAS, T_FMAP, T_NOISE, T_ROUTE, T_EXPERT = 0, 1, 2, 3, 4, 5, 16
+T_X, T_ROUTER, T_BIAS, T_FMAP, T_NOISE, T_ROUTE, T_TIER, T_EXPERT = 0, 1, 2, 3, 4, 5, 6, 16
 # matrix ids inside an expert stream
 M_GATE, M_UP, M_DOWN = 0, 1, 2
 
 MIX_SHARES = (("TERN160", 0.428), ("Q2_0", 0.392), ("Q3", 0.180))
+# every routed format in equal shares (tests of a table that mixes all five)
+MIX_ALL_SHARES = (("TERN160", 0.2), ("Q2_0", 0.2), ("Q3", 0.2), ("MXFP4", 0.2), ("Q8", 0.2))
 
 
 @dataclass(frozen=True)
@@ -63,7 +67,29 @@ WORKLOADS = {
     # 20-layer FP4 stack (no shared expert); 2048 rows is the prefill shape
     "fp4_stack20": Workload("fp4_stack20", 5, 5120, 2304, 384, 6, "MXFP4", None,
                             layers=20, rows=(1, 8, 2048)),
+    # the draft model's MoE layer: 128 routed experts, top-3 ([P1 §1]:
+    # dspark_n_routed_experts 128, dspark_num_experts_per_tok 3), a block of 5
+    # drafted rows (dspark_block_size 5); Q2_0 experts (the draft sidecar is a
+    # 2-bit file, [P3 §三])
+    "draft128": Workload("draft128", 7, 5120, 2304, 128, 3, "Q2_0", "Q2_0", rows=(1, 5)),
+    # the mixed stack under the residency-style selection bias ([P3 §五.3]),
+    # scale 0.5 (the page's default; the bench also runs 0, 0.25 and 1.0)
+    "policy_stack40": Workload("policy_stack40", 8, 5120, 2304, 384, 6, "MIX", "Q8",
+                               layers=40, rows=(1, 7), extra={"policy_scale": 0.5}),
+    # the mixed stack decoded in verify windows of correlated rows, rho chosen
+    # so that a 7-row window touches about 25 distinct experts per layer
+    # ([P1 §3B]: 38,543 + 5,857 expert evaluations in 44 passes of 40 layers)
+    "verify_correlated": Workload("verify_correlated", 9, 5120, 2304, 384, 6, "MIX", "Q8",
+                                  use_bias=True, layers=40, rows=(1, 2, 3, 4, 5, 6, 7, 8),
+                                  extra={"rho": 0.9}),
 }
+
+# Tiers of the residency policy per layer of 384 experts: fast (+1.0), middle
+# (0) and slow (-0.6).  [P3 §五.2] keeps ~1,300-1,600 experts in VRAM, ~6,700
+# in a pinned RAM arena and the rest (~8,700) on NVMe over 40 layers; per
+# layer that is ~36 / ~168 / ~180.  [P3 §五.3]: resident +1.0, NVMe -0.6.
+POLICY_TIERS = (36, 168, 180)
+POLICY_BIAS = (1.0, 0.0, -0.6)
 
 
 def rng(wl, layer, tensor, expert=0):
@@ -91,10 +117,50 @@ def router(wl, layer):
 
 
 def bias(wl, layer):
+    """The layer's selection bias, or None: the residency policy when the
+    workload names a policy scale, else U(-0.6, 1.0) when it uses a bias."""
+    if "policy_scale" in wl.extra:
+        return policy_bias(wl, layer, wl.extra["policy_scale"])
     if not wl.use_bias:
         return None
     g = rng(wl, layer, T_BIAS)
     return g.uniform(-0.6, 1.0, wl.n_experts).astype(np.float32)
+
+
+def policy_tiers(wl, layer):
+    """Tier (0 fast, 1 middle, 2 slow) of every routed expert: the per-layer
+    counts of POLICY_TIERS (scaled to n_experts, remainder to the slow tier)
+    placed by a seeded permutation."""
+    n = wl.n_experts
+    fast = int(np.floor(n * POLICY_TIERS[0] / 384 + 0.5))
+    mid = int(np.floor(n * POLICY_TIERS[1] / 384 + 0.5))
+    tiers = np.array([0] * fast + [1] * mid + [2] * (n - fast - mid), np.int64)
+    return tiers[rng(wl, layer, T_TIER).permutation(n)]
+
+
+def policy_bias(wl, layer, scale):
+    """+1.0 / 0 / -0.6 by tier, times scale, as fp32."""
+    b = np.asarray(POLICY_BIAS, np.float64)[policy_tiers(wl, layer)] * scale
+    return b.astype(np.float32)
+
+
+def correlated_x(wl, layer, rows, rho, stream=0):
+    """A verify window: rows x_r = rho * x_0 + sqrt(1 - rho^2) * z_r (x_0, z_r
+    iid N(0, 1) in fp32, x_0 = z_0), rounded to bf16."""
+    g = rng(wl, layer, T_X, 10_000_000 + stream)
+    z = g.standard_normal((rows, wl.hidden), dtype=np.float32)
+    x = np.float32(rho) * z[:1] + np.float32(np.sqrt(1.0 - rho * rho)) * z
+    x[0] = z[0]
+    return f32_to_bf16_bits(x)
+
+
+def correlated_noise(wl, layer, rows, rho):
+    """Stack noise for a verify window, correlated across rows like the rows."""
+    g = rng(wl, layer, T_NOISE, 1)
+    z = g.standard_normal((rows, wl.hidden), dtype=np.float32)
+    e = np.float32(rho) * z[:1] + np.float32(np.sqrt(1.0 - rho * rho)) * z
+    e[0] = z[0]
+    return e
 
 
 def expert_weights(wl, layer, expert):
@@ -107,19 +173,21 @@ def expert_weights(wl, layer, expert):
     return gate, up, down
 
 
-def mix_counts(n_experts):
-    """Exact per-layer counts for MIX_SHARES; the remainder goes to the last format."""
-    counts = [int(np.floor(n_experts * s + 0.5)) for _, s in MIX_SHARES[:-1]]
+def mix_counts(n_experts, shares=MIX_SHARES):
+    """Exact per-layer counts for the shares; the remainder goes to the last format."""
+    counts = [int(np.floor(n_experts * s + 0.5)) for _, s in shares[:-1]]
     counts.append(n_experts - sum(counts))
     return counts
 
 
 def format_map(wl, layer):
-    """List of format names, one per routed expert."""
-    if wl.routed_fmt != "MIX":
+    """List of format names, one per routed expert ("MIX": the ternary / Q2_0 /
+    Q3 shares; "MIXALL": all five formats in equal shares)."""
+    if wl.routed_fmt not in ("MIX", "MIXALL"):
         return [wl.routed_fmt] * wl.n_experts
+    shares = MIX_SHARES if wl.routed_fmt == "MIX" else MIX_ALL_SHARES
     names = []
-    for (name, _), c in zip(MIX_SHARES, mix_counts(wl.n_experts)):
+    for (name, _), c in zip(shares, mix_counts(wl.n_experts, shares)):
         names += [name] * c
     perm = rng(wl, layer, T_FMAP).permutation(wl.n_experts)
     return [names[i] for i in perm]

@@ -71,7 +71,8 @@ typedef enum {
   MOE_EFORMAT = -3,     /* unknown format tag                                */
   MOE_EWORKSPACE = -4,  /* workspace smaller than moe_workspace_bytes()      */
   MOE_EDEVICE = -5,     /* a HIP launch or runtime call failed               */
-  MOE_ECODE = -6        /* moe_unpack met an invalid code (ternary byte > 242, e8m0 255) */
+  MOE_ECODE = -6,       /* moe_unpack met an invalid code (ternary byte > 242, e8m0 255) */
+  MOE_ETIMEOUT = -7     /* moe_workspace_status: a hand-off wait of a fused call gave up */
 } moe_status;
 
 typedef enum {
@@ -137,7 +138,15 @@ typedef struct {
   int32_t inter;      /* I: 2304 / 256                                          */
   int32_t n_experts;  /* E routed experts: 384 / 16                             */
   int32_t top_k;      /* k: 6 / 2                                               */
+  uint32_t flags;     /* MOE_ACT_* bits; 0 for none                             */
 } moe_dims;
+
+/* moe_dims.flags: on the many-row path (rows > MOE_MAX_DECODE_ROWS), MXFP4
+ * experts run on the scaled matrix cores with the activations quantised to
+ * MXFP8 (as moe_quant_mxfp8).  Without it, and for every other format, the
+ * many-row path runs the decode tiles on unquantised activations.  Ignored
+ * by the decode path.  Any other bit: MOE_EINVAL. */
+#define MOE_ACT_MXFP8 1u
 
 /* One expert: its format and the byte offsets of its three packed matrices
  * inside the `weights` buffer: gate [I x H], up [I x H], down [H x I].  Each
@@ -149,9 +158,13 @@ typedef struct {
 } moe_expert_ref;
 
 /* Supported shapes: (hidden, inter) = (5120, 2304) or (512, 256);
- * 1 <= top_k <= MOE_MAX_TOP_K, top_k <= n_experts <= 512,
- * rows * top_k <= 64, rows <= MOE_MAX_DECODE_ROWS.  Returns 0 for
- * unsupported dims. */
+ * 1 <= top_k <= MOE_MAX_TOP_K, top_k <= n_experts <= 512; on the decode path
+ * rows <= MOE_MAX_DECODE_ROWS and rows * top_k <= 64, on the many-row path
+ * rows <= MOE_MAX_PREFILL_ROWS.  Returns 0 for unsupported dims or flags.
+ * Every workspace begins with the same area, sized by the dims alone, that
+ * holds the fused decode launch's tagged words; every other use of the
+ * workspace lies past it, so one workspace may serve calls of any kind and
+ * any row count in turn. */
 size_t moe_workspace_bytes(const moe_dims* dims, int32_t rows);
 
 /* Host check of an expert table (host memory) against the dims and the size
@@ -198,13 +211,20 @@ int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, vo
  *   y          [rows x H] fp32, device, out (overwritten)
  * Deterministic: the same inputs give bitwise the same y.
  * rows <= MOE_MAX_DECODE_ROWS: the decode path, any formats.
- * MOE_MAX_DECODE_ROWS < rows <= MOE_MAX_PREFILL_ROWS: the prefill path on the
- * scaled matrix cores.  x is quantised to MXFP8 (as moe_quant_mxfp8) for the
- * gate/up products; h = silu(W_gate x) * (W_up x) is rounded to f16 for the
- * down products (f16 x MXFP4 on the matrix cores); every selected expert
- * must be MXFP4 (a row that selects another format comes out NaN); shared
- * must be NULL (else MOE_ESHAPE).  The workspace is moe_workspace_bytes(dims,
- * rows) (about rows * top_k * (hidden * 4 + inter) bytes). */
+ * MOE_MAX_DECODE_ROWS < rows <= MOE_MAX_PREFILL_ROWS: the many-row path
+ * ("[Strata] DeepSeek V4.1 Flash on a single 4090", section 4: prefill runs
+ * the experts as matrix products).  Pairs (row, expert) are grouped by
+ * expert in ascending (expert, pair) order, then:
+ *   - with MOE_ACT_MXFP8 in dims->flags, an MXFP4 expert runs on the scaled
+ *     matrix cores in chunks of 64 pairs: x quantised to MXFP8 (as
+ *     moe_quant_mxfp8) for gate/up, h = silu(W_gate x) * (W_up x) rounded to
+ *     f16 for down (f16 x MXFP4);
+ *   - every other expert (any format, MXFP4 too without the flag) and the
+ *     shared expert run the decode tiles on unquantised activations, 8 pairs
+ *     of one expert per work entry, h in fp32.
+ * y[r] = the row's expert outputs, weighted, in ascending expert id, then the
+ * shared expert.  The workspace is moe_workspace_bytes(dims, rows) (about
+ * rows * top_k * (hidden * 4 + inter * 6) bytes). */
 int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const int32_t* idx,
                    const float* wts, const void* weights, const moe_expert_ref* experts,
                    const moe_expert_ref* shared, float* y, void* ws, size_t ws_bytes,
@@ -217,12 +237,19 @@ int moe_expert_ffn(const moe_dims* dims, const void* x_bf16, int32_t rows, const
  * (the shared expert's gate/up tiles, the routed gate/up items, then the
  * down items), then a fixed-order combine.  The shared expert streams while
  * the selection is made and down weights stream while h is still being
- * computed.  idx and wts are outputs as in moe_route.
+ * computed.  idx and wts are outputs as in moe_route (NULL: not written).
  * The launch holds at most one residency round of workers (the occupancy the
  * runtime reports for the kernel, times the compute units), since a down item
- * may wait on a gate/up item of any worker: a kernel on another stream that
- * keeps compute units busy meanwhile can only delay it.  Should a hand-off ever fail to arrive, its
- * waits end after a bounded spin and y comes out NaN. */
+ * may wait on a gate/up item of any worker.  The launch assumes that its
+ * workgroups start in id order and that, once the router and selection
+ * workgroups are done, every worker is resident; a kernel on another stream
+ * that holds compute units can delay that.  Every wait on another
+ * workgroup's words is bounded (moe_set_spin_limit): a wait that gives up
+ * poisons what it feeds with NaN (the routing weights, h, the partial
+ * outputs, y) and records the call in the workspace's error word, so such a
+ * call's y is NaN wherever the failure reached, and moe_workspace_status
+ * reports it.  Status MOE_OK means the launch was made, not that every wait
+ * succeeded. */
 int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
               const float* sel_bias, const void* weights, const moe_expert_ref* experts,
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
@@ -266,6 +293,14 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
                      int32_t rows, void* x_all, const float* noise, float* y_all,
                      int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
 
+/* Whether a hand-off wait of any fused call (moe_layer, moe_layer_profiled,
+ * moe_stack_decode) on this workspace gave up since the workspace was
+ * zero-filled or last queried.  Synchronises `stream` (the host blocks until
+ * every call queued on it has finished), reads the workspace's error word and
+ * clears it.  Returns MOE_OK, MOE_ETIMEOUT (some call's y holds NaN from the
+ * failure), MOE_EINVAL (null ws or ws_bytes below 16) or MOE_EDEVICE. */
+int moe_workspace_status(void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Test aid: the fused launch's hand-off waits.                              */
 /* ------------------------------------------------------------------------ */
@@ -273,11 +308,12 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
 /* Every wait of one moe_layer / moe_stack_decode launch on words published
  * by another workgroup of the same launch gives up after `polls` polls
  * (default 65536, tens of ms): the launch then still drains, the failure is
- * recorded in the workspace's error word, the call's y is NaN, and a worker
- * whose wait for the selection gave up computes with expert 0 instead of
- * reading stale entries.  0 makes every wait give up at once, which lets a
- * test reach that path without a hung producer.  Process-wide, read at each
- * launch.  Returns the previous value, or MOE_EINVAL for polls < 0. */
+ * recorded in the workspace's error word and poisons the data it feeds with
+ * NaN (a worker whose wait for the selection gave up computes with expert 0,
+ * weight NaN, instead of reading stale entries).  0 makes every wait give up
+ * at once, which lets a test reach that path without a hung producer.
+ * Process-wide, read at each launch.  Returns the previous value, or
+ * MOE_EINVAL for polls < 0. */
 int32_t moe_set_spin_limit(int32_t polls);
 
 /* ------------------------------------------------------------------------ */
@@ -285,9 +321,9 @@ int32_t moe_set_spin_limit(int32_t polls);
 /* ------------------------------------------------------------------------ */
 
 /* The streaming-read ceiling against which the layer's HBM rate is also
- * reported ("DeepSeek-V4.1-Flash served three ways on 4xL20", section 7: a
- * bandwidth figure is judged against what the device reaches on a plain
- * stream).  Reads the first floor(bytes / 16) 16-byte chunks of `buf` with
+ * reported ("DeepSeek-V4.1-Flash served three ways on 4xL20", section 6: the
+ * bandwidth a workload sees falls short of the micro-benchmark figure, so a
+ * rate is judged against what the device reaches on a plain stream).  Reads the first floor(bytes / 16) 16-byte chunks of `buf` with
  * one 16-byte load per lane and `unroll` loads in flight per lane per
  * iteration, grid-striding over `grid` workgroups of 256 threads, and
  * writes one xor checksum per thread to `sink` so that no load is dropped.

@@ -130,21 +130,33 @@ def expert_ffn_loops(x, w_gate, w_up, w_down):
     return out
 
 
+def combine_outputs(shape, idx, w, outputs, shared_out=None):
+    """The weighted sum of given expert outputs:
+    y_r = sum_{e in S_r, ascending e} w_{r,e} * outputs[e][i]  +  shared_out[r],
+    where outputs[e][i] is expert e's output for the i-th row that selects e
+    (rows in ascending order, as np.nonzero(idx == e) lists them)."""
+    y = np.zeros(shape)
+    w = np.asarray(w, np.float64)
+    for e in np.unique(idx):
+        rows, slots = np.nonzero(idx == e)
+        y[rows] += w[rows, slots][:, None] * outputs[int(e)]
+    if shared_out is not None:
+        y += shared_out
+    return y
+
+
 def combine(x, idx, w, expert_fn, shared=None):
     """y_r = sum_{e in S_r, ascending e} w_{r,e} * E_e(x_r)  +  shared(x_r).
 
     expert_fn(e) -> (Wg, Wu, Wd) decoded fp64 matrices; it is called once per
     distinct selected expert.  shared: (Wg, Wu, Wd) or None."""
     x = np.asarray(x, np.float64)
-    y = np.zeros_like(x)
+    outs = {}
     for e in np.unique(idx):
-        rows, slots = np.nonzero(idx == e)
-        mats = expert_fn(int(e))
-        o = expert_ffn(x[rows], *mats)
-        y[rows] += w[rows, slots][:, None] * o
-    if shared is not None:
-        y += expert_ffn(x, *shared)
-    return y
+        rows, _ = np.nonzero(idx == e)
+        outs[int(e)] = expert_ffn(x[rows], *expert_fn(int(e)))
+    return combine_outputs(x.shape, idx, w, outs,
+                           expert_ffn(x, *shared) if shared is not None else None)
 
 
 def moe_layer(x, w_router, k, expert_fn, shared=None, bias=None):
@@ -224,6 +236,31 @@ def prefill_layer(x, idx, w, expert_fn):
         rows, cols = np.nonzero(idx == e)
         o = expert_ffn(xq[rows], *expert_fn(e))
         y[rows] += np.asarray(w, np.float64)[rows, cols][:, None] * o
+    return y
+
+
+def many_row_layer(x, idx, w, expert_fn, fmt_of, act_mxfp8, shared=None):
+    """The many-row call for a given routing, with experts of any format.
+
+    y[r] = sum over the row's experts in ascending id of w * FFN_e(x_e[r])
+           + FFN_shared(x[r]) (weight 1, when there is a shared expert),
+    where x_e = Q_MXFP8(x) for an MXFP4 expert when act_mxfp8 is set (those
+    experts run on the fp8 x fp4 matrix cores) and x_e = x otherwise (the
+    decode tiles, on unquantised activations; the shared expert always).
+    The pages run prefill as matrix products ([P3 §四]); which activations
+    each expert sees follows the library's flag and is this reading's choice.
+    fmt_of(e) -> format name of routed expert e."""
+    x = np.asarray(x, np.float64)
+    xq = quant_mxfp8(x)[0] if act_mxfp8 else None
+    y = np.zeros_like(x)
+    idx = np.asarray(idx)
+    wv = np.asarray(w, np.float64)
+    for e in sorted(set(idx.reshape(-1).tolist())):
+        rows, cols = np.nonzero(idx == e)
+        xin = xq if (act_mxfp8 and fmt_of(e) == "MXFP4") else x
+        y[rows] += wv[rows, cols][:, None] * expert_ffn(xin[rows], *expert_fn(e))
+    if shared is not None:
+        y += expert_ffn(x, *shared)
     return y
 
 

@@ -40,7 +40,7 @@ def test_tiny_layer(rows, stream):
     G.check_routing(gi, gw, idx, w, gap, logits)
     ref = G.oracle_y(wl, 0, x, idx, w, list(range(rows)))
     err = G.rel_l2_rows(gy, ref)
-    _say("  rel L2 per row", err)
+    _say("  rel L2 per row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
 
 
@@ -104,6 +104,7 @@ def test_given_up_waits_give_nan_and_the_next_call_recovers():
 
     y_ok = run()
     assert np.all(np.isfinite(y_ok))
+    assert L.moe_workspace_status(ws) == L.MOE_OK
     prev = L.moe_set_spin_limit(0)
     try:
         y_fail = run()
@@ -111,7 +112,10 @@ def test_given_up_waits_give_nan_and_the_next_call_recovers():
         L.moe_set_spin_limit(prev)
     _say("NaN fraction with spin limit 0:", float(np.isnan(y_fail).mean()))
     assert np.all(np.isnan(y_fail))
+    assert L.moe_workspace_status(ws) == L.MOE_ETIMEOUT      # reported once, then cleared
+    assert L.moe_workspace_status(ws) == L.MOE_OK
     assert np.array_equal(run(), y_ok)
+    assert L.moe_workspace_status(ws) == L.MOE_OK
 
 
 def test_route_only_and_ffn_only_match_layer():
@@ -158,7 +162,7 @@ def test_tiny_selection_limits():
     gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), 8)
     G.check_routing(gi, gw, idx, w, gap, logits)
     err = G.rel_l2_rows(gy, G.oracle_y(wl, 0, x, idx, w, list(range(8))))
-    _say("  rel L2 per row", err)
+    _say("  rel L2 per row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
 
 
@@ -173,7 +177,7 @@ def _real_case(wl, rows, stream, check_rows):
     G.check_routing(gi, gw, idx, w, gap, logits)
     ref = G.oracle_y(wl, 0, x, idx, w, check_rows)
     err = G.rel_l2_rows(gy[check_rows], ref)
-    _say("  rel L2 per checked row", err)
+    _say("  rel L2 per checked row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
     return gy
 
@@ -182,9 +186,76 @@ def test_decode_q2_layer_one_row():
     _real_case(synth.WORKLOADS["decode_q2"], 1, 0, [0])
 
 
-@pytest.mark.parametrize("rows,check", [(1, [0]), (5, [2]), (8, [0, 7])])
-def test_mixed_verify_layer(rows, check):
-    _real_case(synth.WORKLOADS["mixed_verify"], rows, rows, check)
+def _every_row_case(wl, rows, stream, twice=True):
+    """A real-shape layer holding exactly the experts the rows select, every
+    row checked against the oracle; with `twice`, a second call on the same
+    workspace must give bitwise the same y, idx and weights."""
+    xbits = synth.x_bf16(wl, 0, rows, stream)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    _say(f"{wl.name}: rows {rows}, {len(np.unique(idx))} distinct experts, every row checked")
+    dl, ref = G.materialized_layer_and_oracle(wl, 0, x, idx, w)
+    xd = G.device_inputs(wl, 0, xbits)
+    gi, gw, gy, ws = G.run_layer(dl, xd, rows)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    err = G.rel_l2_rows(gy, ref)
+    _say("  rel L2 per row", G.fmt_err(err))
+    assert np.all(err <= G.REL_L2_TOL)
+    if twice:
+        idx2 = torch.zeros((rows, wl.top_k), dtype=torch.int32, device="cuda")
+        wts2 = torch.zeros((rows, wl.top_k), dtype=torch.float32, device="cuda")
+        y2 = torch.zeros((rows, wl.hidden), dtype=torch.float32, device="cuda")
+        L.moe_layer(dl.dims, xd, rows, dl.router, dl.bias, dl.weights, dl.experts, dl.shared,
+                    idx2, wts2, y2, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx2.cpu().numpy(), gi)
+        assert np.array_equal(wts2.cpu().numpy(), gw)
+        assert np.array_equal(y2.cpu().numpy(), gy), "a second identical call changed y"
+        assert L.moe_workspace_status(ws) == L.MOE_OK
+
+
+@pytest.mark.parametrize("rows", [1, 5, 8])
+def test_mixed_verify_layer_every_row(rows):
+    """The mixed-format verify layer with its selection bias (ternary / Q2_0 /
+    Q3 experts, a Q8 shared expert) at rows 1, 5 and 8: every row."""
+    _every_row_case(synth.WORKLOADS["mixed_verify"], rows, rows)
+
+
+@pytest.mark.parametrize("rows", [1, 8])
+def test_fp4_layer_fused_every_row(rows):
+    """MXFP4 experts through the fused launch (moe_layer), one layer of the
+    FP4 stack (no shared expert), at rows 1 and 8: every row."""
+    _every_row_case(synth.WORKLOADS["fp4_stack20"], rows, 40 + rows)
+
+
+def test_many_row_call_then_fused_call_share_a_workspace():
+    """A many-row call writes its pair lists and chunk tables into the
+    workspace; a fused decode call on the same workspace right after must not
+    take any of those words for its own hand-off words (the tagged area sits
+    apart from everything else).  55 rows then 1 row, real shape."""
+    wl = synth.WORKLOADS["fp4_stack20"]
+    xb1 = synth.x_bf16(wl, 0, 1, 77)
+    x1, idx1, w1, logits, gap = G.oracle_route(wl, 0, xb1)
+    dl, ref = G.materialized_layer_and_oracle(wl, 0, x1, idx1, w1, flags=L.MOE_ACT_MXFP8)
+    ws = torch.zeros(max(L.workspace_bytes(dl.dims, 55), L.workspace_bytes(dl.dims, 1)),
+                     dtype=torch.uint8, device="cuda")
+    ri, rw = synth.zipf_routing(wl, 0, 55)
+    y55 = torch.zeros((55, wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_expert_ffn(dl.dims, G.device_inputs(wl, 0, synth.x_bf16(wl, 0, 55, 78)), 55,
+                     torch.from_numpy(ri).cuda(), torch.from_numpy(rw).cuda(), dl.weights,
+                     dl.experts, None, y55, ws)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(y55.cpu().numpy()))
+    idx = torch.zeros((1, wl.top_k), dtype=torch.int32, device="cuda")
+    wts = torch.zeros((1, wl.top_k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((1, wl.hidden), dtype=torch.float32, device="cuda")
+    L.moe_layer(dl.dims, G.device_inputs(wl, 0, xb1), 1, dl.router, dl.bias, dl.weights,
+                dl.experts, dl.shared, idx, wts, y, ws)
+    torch.cuda.synchronize()
+    G.check_routing(idx.cpu().numpy(), wts.cpu().numpy(), idx1, w1, gap, logits)
+    err = G.rel_l2_rows(y.cpu().numpy(), ref)
+    _say("  rel L2", G.fmt_err(err))
+    assert np.all(err <= G.REL_L2_TOL)
+    assert L.moe_workspace_status(ws) == L.MOE_OK
 
 
 @pytest.mark.parametrize("fmt", ["TERN160", "Q2_0", "Q3", "MXFP4", "Q8"])
@@ -208,7 +279,7 @@ def test_expert_ffn_each_format_real_shape(fmt):
     torch.cuda.synchronize()
     ref = G.oracle_y(wl, 0, x, idx, w32.astype(np.float64), list(range(rows)))
     err = G.rel_l2_rows(y.cpu().numpy(), ref)
-    _say(f"  {fmt}: rel L2 per row", err)
+    _say(f"  {fmt}: rel L2 per row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
 
 
@@ -234,3 +305,36 @@ def test_fused_layer_matches_split_calls_real_shape():
     assert np.array_equal(wts2.cpu().numpy(), gw)
     np.testing.assert_allclose(y2.cpu().numpy(), gy, rtol=1e-6, atol=1e-6)
     G.check_routing(gi, gw, idx, w, gap, logits)
+
+
+# ------------------------------------------------------------------ workloads of the next steps
+@pytest.mark.parametrize("rows", [1, 5])
+def test_draft_layer_every_row(rows):
+    """The draft model's MoE layer: 128 experts, top-3, a Q2_0 shared expert."""
+    _every_row_case(synth.WORKLOADS["draft128"], rows, 60 + rows)
+
+
+@pytest.mark.parametrize("scale,rows", [(0.5, 7), (1.0, 1)])
+def test_residency_policy_bias_every_row(scale, rows):
+    """The mixed layer under the residency-style selection bias (+1.0 fast /
+    -0.6 slow tier, times the scale): ids exact, weights the unbiased softmax."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["policy_stack40"], layers=1, extra={"policy_scale": scale})
+    _every_row_case(wl, rows, 70 + rows, twice=False)
+
+
+def test_correlated_verify_window_every_row():
+    """A verify window of 7 correlated rows (rho 0.9): rows share experts, so
+    slots serve several rows; every row checked."""
+    wl = synth.WORKLOADS["verify_correlated"]
+    rows = 7
+    xbits = synth.correlated_x(wl, 0, rows, 0.9, 5)
+    x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
+    _say(f"correlated window: {len(np.unique(idx))} distinct experts for {rows} rows")
+    assert len(np.unique(idx)) < rows * wl.top_k
+    dl, ref = G.materialized_layer_and_oracle(wl, 0, x, idx, w)
+    gi, gw, gy, ws = G.run_layer(dl, G.device_inputs(wl, 0, xbits), rows)
+    G.check_routing(gi, gw, idx, w, gap, logits)
+    err = G.rel_l2_rows(gy, ref)
+    _say("  rel L2 per row", G.fmt_err(err))
+    assert np.all(err <= G.REL_L2_TOL)

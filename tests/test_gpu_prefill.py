@@ -1,7 +1,10 @@
-"""GPU parity of the prefill path: moe_expert_ffn with more than 8 rows runs
-MXFP4 experts on the matrix cores: gate/up with MXFP8 x on the scaled fp8 x
-fp4 instruction, down with f16 h.  The oracle quantises x the same way
-(oracle.moe.prefill_layer) and computes the rest in fp64.
+"""GPU parity of the many-row path: moe_expert_ffn with more than 8 rows.
+
+With MOE_ACT_MXFP8, MXFP4 experts run on the matrix cores: gate/up with
+MXFP8 x on the scaled fp8 x fp4 instruction, down with f16 h; the oracle
+quantises x the same way (oracle.moe.prefill_layer / many_row_layer) and
+computes the rest in fp64.  Every other expert (any format, and MXFP4 without
+the flag) and the shared expert run the decode tiles on unquantised x.
 
 Bar: the MXFP8 quantiser bit-exact; y within 1e-3 relative L2 per row."""
 
@@ -64,12 +67,13 @@ def test_quant_mxfp8_bit_exact():
     np.testing.assert_array_equal(got, want)
 
 
-def _prefill(dl, xbits, idx, w, rows):
-    d = dl.dims
+def _prefill(dl, xbits, idx, w, rows, flags=L.MOE_ACT_MXFP8, shared=None):
+    wl = dl.wl
+    d = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k, flags)
     ws = LY.workspace(d, rows)
     y = torch.zeros((rows, dl.wl.hidden), dtype=torch.float32, device="cuda")
     L.moe_expert_ffn(d, G.device_inputs(dl.wl, 0, xbits), rows, torch.from_numpy(idx).cuda(),
-                     torch.from_numpy(w).cuda(), dl.weights, dl.experts, None, y, ws)
+                     torch.from_numpy(w).cuda(), dl.weights, dl.experts, shared, y, ws)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
@@ -89,7 +93,7 @@ def test_tiny_prefill_every_row():
     ref = OM.prefill_layer(OM.bf16_to_f64(xbits), idx, w.astype(np.float64),
                            lambda e: G.oracle_expert(wl, 0, e))
     err = G.rel_l2_rows(y, ref)
-    _say("max rel L2", err.max())
+    _say("max rel L2", f"{err.max():.2e}")
     assert np.all(err <= G.REL_L2_TOL)
     assert np.array_equal(y, _prefill(dl, xbits, idx, w, R))      # bitwise reproducible
 
@@ -114,15 +118,57 @@ def test_real_shape_prefill_sampled_rows():
     ref = OM.prefill_layer(x[check], idx[check], w[check].astype(np.float64),
                            lambda e: G.oracle_expert(wl, 0, e))
     err = G.rel_l2_rows(y[check], ref)
-    _say("rel L2 per checked row", err)
+    _say("rel L2 per checked row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
 
 
-def test_prefill_rows_of_a_non_mxfp4_expert_are_nan():
-    wl = synth.Workload("tiny_q2_prefill", 31, 512, 256, 16, 2, "Q2_0", None, rows=(16,))
-    R = 16
-    xbits = synth.x_bf16(wl, 0, R)
-    idx, w = synth.zipf_routing(wl, 0, R)
+def _tiny_many_rows(name, key, fmt, rows, flags, shared_fmt):
+    wl = synth.Workload(name, key, 512, 256, 16, 2, fmt, shared_fmt, rows=(rows,))
+    xbits = synth.x_bf16(wl, 0, rows)
+    idx, w = synth.zipf_routing(wl, 0, rows)
     dl = LY.DeviceLayer(wl, 0, materialize=range(wl.n_experts))
-    y = _prefill(dl, xbits, idx, w, R)
-    assert np.all(np.isnan(y))
+    fm = synth.format_map(wl, 0)
+    _say(f"{name}: {rows} rows, formats {sorted(set(fm))}, flags {flags}, shared {shared_fmt}")
+    y = _prefill(dl, xbits, idx, w, rows, flags, dl.shared)
+    shared = G.oracle_expert(wl, 0, wl.n_experts) if shared_fmt else None
+    ref = OM.many_row_layer(OM.bf16_to_f64(xbits), idx, w.astype(np.float64),
+                            lambda e: G.oracle_expert(wl, 0, e), lambda e: fm[e],
+                            bool(flags & L.MOE_ACT_MXFP8), shared)
+    err = G.rel_l2_rows(y, ref)
+    _say("  max rel L2", f"{err.max():.2e}")
+    assert np.all(err <= G.REL_L2_TOL)
+    assert np.array_equal(y, _prefill(dl, xbits, idx, w, rows, flags, dl.shared))   # bitwise again
+
+
+def test_tiny_many_rows_generic_mixed_formats_with_shared():
+    """Ternary / Q2_0 / Q3 experts and a Q8 shared expert, 40 rows: every pair
+    runs the decode tiles (entries of up to 8 pairs of one expert)."""
+    _tiny_many_rows("tiny_mix_many", 32, "MIX", 40, 0, "Q8")
+
+
+def test_tiny_many_rows_all_formats_with_the_flag():
+    """All five formats mixed, 96 rows, MOE_ACT_MXFP8: MXFP4 experts on the
+    matrix cores (quantised x), the others and the shared expert on the
+    decode tiles (unquantised x), one combine in ascending expert id."""
+    _tiny_many_rows("tiny_all_many", 33, "MIXALL", 96, L.MOE_ACT_MXFP8, "Q2_0")
+
+
+def test_tiny_many_rows_mxfp4_without_the_flag_is_exact():
+    """MXFP4 experts without the flag: the decode tiles on unquantised x."""
+    _tiny_many_rows("tiny_fp4_generic", 34, "MXFP4", 24, 0, None)
+
+
+def test_real_shape_many_rows_generic_sampled():
+    """The mixed-format layer (with its Q8 shared expert) at 24 rows on the
+    generic path; the first, a middle and the last row checked."""
+    wl = synth.WORKLOADS["mixed_verify"]
+    R = 24
+    xbits = synth.x_bf16(wl, 0, R, 9)
+    idx, w = synth.zipf_routing(wl, 0, R)
+    check = [0, 11, R - 1]
+    x = OM.bf16_to_f64(xbits)
+    dl, ref = G.materialized_layer_and_oracle(wl, 0, x[check], idx[check], w[check].astype(np.float64))
+    y = _prefill(dl, xbits, idx, w, R, 0, dl.shared)
+    err = G.rel_l2_rows(y[check], ref)
+    _say("rel L2 per checked row", G.fmt_err(err))
+    assert np.all(err <= G.REL_L2_TOL)

@@ -40,14 +40,17 @@ def _run_stack(wl, layers, rows, stream=0):
             idx_all.cpu().numpy(), wts_all.cpu().numpy())
 
 
-def _check_layers(wl, layers, rows, check_rows, stream=0):
+def _check_layers(wl, layers, rows, check_rows, stream=0, parallel=False):
     xs, noise, ys, idxs, wtss = _run_stack(wl, layers, rows, stream)
     for l, dl in enumerate(layers):
         x, idx, w, logits, gap = G.oracle_route(wl, l, xs[l])
         G.check_routing(idxs[l], wtss[l], idx, w, gap, logits)
-        ref = G.oracle_y_for(dl, x, idx, w, check_rows)
+        if parallel:
+            ref = G.oracle_y_parallel(dl, x[check_rows], idx[check_rows], w[check_rows])
+        else:
+            ref = G.oracle_y_for(dl, x, idx, w, check_rows)
         err = G.rel_l2_rows(ys[l][check_rows], ref)
-        _say(f"  layer {l}: rel L2 {np.array2string(err, precision=2)}")
+        _say(f"  layer {l}: rel L2 {G.fmt_err(err)}")
         assert np.all(err <= G.REL_L2_TOL)
         nxt = OM.chain_next(ys[l], noise[l])
         np.testing.assert_array_equal(OM.bf16_to_f64(xs[l + 1]), nxt)
@@ -62,11 +65,24 @@ def test_tiny_stack_chained(rows):
 
 
 def test_mixed_stack_real_shape_three_layers():
-    """Three layers of the 40-layer mixed stack at rows 7; unselected slots are
-    pool-filled, every checked expert's weights are regenerated for the oracle."""
+    """Three layers of the 40-layer mixed stack at rows 7, every row of every
+    layer; slots are pool-filled, every selected expert's weights are
+    regenerated for the oracle."""
     base = synth.WORKLOADS["stack40_mixed"]
     rows, n = 7, 3
     _say(f"mixed stack: {n} layers of {base.name}, rows {rows}")
     pool = LY.make_pool(base, 0, ["TERN160", "Q2_0", "Q3"], 8)
     layers = [LY.DeviceLayer(base, l, materialize=(), pool=pool) for l in range(n)]
-    _check_layers(base, layers, rows, [rows - 1], stream=3)
+    _check_layers(base, layers, rows, list(range(rows)), stream=3, parallel=True)
+
+
+@pytest.mark.parametrize("rows", [1, 8])
+def test_fp4_stack_real_shape_three_layers(rows):
+    """Three layers of the FP4 stack (MXFP4 experts, no shared expert) chained
+    through moe_stack_decode at rows 1 and 8, every row of every layer."""
+    base = synth.WORKLOADS["fp4_stack20"]
+    n = 3
+    _say(f"fp4 stack: {n} layers of {base.name}, rows {rows}")
+    pool = LY.make_pool(base, 0, ["MXFP4"], 12)
+    layers = [LY.DeviceLayer(base, l, materialize=(), pool=pool) for l in range(n)]
+    _check_layers(base, layers, rows, list(range(rows)), stream=50 + rows, parallel=True)

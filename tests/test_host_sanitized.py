@@ -1,0 +1,34 @@
+"""The host code of libmoe (packer and argument / workspace validation) under
+AddressSanitizer and UndefinedBehaviorSanitizer: tests/host_check.cpp built
+with g++ together with pack.cpp and host_api.cpp (no HIP code is involved)
+and run on the CPU."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_moe_expert_02_amd", "csrc")
+
+
+def test_host_code_under_asan_and_ubsan(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ is not installed")
+    exe = tmp_path / "host_check"
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "host_check.cpp"),
+           os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "host_api.cpp"),
+           "-pthread", "-o", str(exe)]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stdout + build.stderr
+    # verify_asan_link_order=0: the environment may preload other libraries
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "host checks ok" in run.stdout

@@ -228,3 +228,38 @@ def test_zipf_routing_input_shape_and_skew():
     np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-6)
     counts = np.bincount(idx.reshape(-1), minlength=384)
     assert counts.max() > 20 * counts.mean() and counts.mean() == 32
+
+
+# ---------------------------------------------------------------- router GEMV
+def test_router_logits_hand_worked(golden):
+    """Logits of small integer / power-of-two inputs equal the sums worked by
+    hand in the fixture (pins the x . Wr^T orientation: a transposed operand
+    would score expert e with column e)."""
+    g = golden("router_worked.json")["small"]
+    got = M.router_logits(np.array(g["x"]), np.array(g["w_router"], np.float32))
+    assert got.shape == (3, 3)
+    assert np.array_equal(got, np.array(g["logits"]))
+
+
+def test_router_logits_one_hot_rows_read_one_router_column():
+    """x = unit vector at h gives logits[e] = Wr[e, h] exactly, for every h."""
+    rng = np.random.default_rng(3)
+    wr = (rng.standard_normal((16, 24)) * 0.02).astype(np.float32)
+    x = np.eye(24)
+    assert np.array_equal(M.router_logits(x, wr), wr.T.astype(np.float64))
+
+
+def test_router_logits_accumulate_beyond_fp32(golden):
+    """The sums are fp64: a logit that needs 31 significant bits comes out
+    exact, and a sum of 2^24, 1, 1, -2^24 is 2.  The same inputs summed in
+    fp32 (the slip this pin is meant to catch) give 1.0 and 0.0."""
+    g = golden("router_worked.json")
+    for case in ("beyond_fp32", "cancellation"):
+        x = np.array(g[case]["x"])
+        wr = np.array(g[case]["w_router"], np.float32)
+        assert M.router_logits(x, wr)[0, 0] == g[case]["logit"]
+        # a planted mistake: the same sum accumulated left to right in fp32
+        acc = np.float32(0.0)
+        for xv, wv in zip(x[0].astype(np.float32), wr[0]):
+            acc = np.float32(acc + np.float32(xv * wv))
+        assert float(acc) != g[case]["logit"]

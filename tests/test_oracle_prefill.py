@@ -56,3 +56,36 @@ def test_prefill_rows_are_independent_and_weighted():
         xq, _ = OM.quant_mxfp8(x[r:r + 1])
         want = sum(w[r, j] * OM.expert_ffn(xq, *experts[idx[r, j]])[0] for j in np.argsort(idx[r]))
         np.testing.assert_allclose(y[r], want, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- many-row layer, any format
+def test_many_row_layer_without_the_flag_is_the_decode_layer():
+    """No MXFP8 activations: the many-row layer is the decode layer's weighted
+    sum on the unquantised rows, for every format, shared expert included."""
+    rng, experts, idx, w = _setup(4)
+    x = rng.standard_normal((7, 64))
+    shared = _expert(rng, 64, 64)
+    y = OM.many_row_layer(x, idx, w, lambda e: experts[e], lambda e: "MXFP4", False, shared)
+    ref = OM.combine(x, idx, w, lambda e: experts[e], shared)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_many_row_layer_all_mxfp4_with_the_flag_is_the_prefill_layer():
+    rng, experts, idx, w = _setup(5)
+    x = rng.standard_normal((7, 64))
+    y = OM.many_row_layer(x, idx, w, lambda e: experts[e], lambda e: "MXFP4", True)
+    np.testing.assert_allclose(y, OM.prefill_layer(x, idx, w, lambda e: experts[e]), rtol=1e-12, atol=1e-14)
+
+
+def test_many_row_layer_mixed_formats_split_by_format():
+    """With the flag, a table mixing MXFP4 and other experts is the sum of the
+    MXFP4 experts' prefill layer and the other experts' decode layer: split
+    the routing by format (zero weight where the other kind is selected)."""
+    rng, experts, idx, w = _setup(6, E=6, k=3)
+    x = rng.standard_normal((7, 64))
+    fmts = ["MXFP4", "Q2_0", "MXFP4", "TERN160", "Q3", "MXFP4"]
+    y = OM.many_row_layer(x, idx, w, lambda e: experts[e], lambda e: fmts[e], True)
+    is_fp4 = np.vectorize(lambda e: fmts[e] == "MXFP4")(idx)
+    part_fp4 = OM.prefill_layer(x, idx, np.where(is_fp4, w, 0.0), lambda e: experts[e])
+    part_rest = OM.combine(x, idx, np.where(is_fp4, 0.0, w), lambda e: experts[e])
+    np.testing.assert_allclose(y, part_fp4 + part_rest, rtol=1e-12, atol=1e-13)
