@@ -26,7 +26,7 @@ MAX_TOP_K = 8
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
            "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
-           "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status")
+           "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status", "moe_layer_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -86,6 +86,8 @@ def lib():
         L.moe_expert_ffn.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_layer.restype = ctypes.c_int
         L.moe_layer.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_layer_noalloc.restype = ctypes.c_int
+        L.moe_layer_noalloc.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.moe_layer_profiled.restype = ctypes.c_int
         L.moe_layer_profiled.argtypes = [dims_p, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          vp, vp, i32]
@@ -189,6 +191,13 @@ def moe_layer(d, x, rows, w_router, bias, weights, experts, shared, idx, wts, y,
         ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router), _ptr(bias), _ptr(weights),
         _ptr(experts), _ptr(shared), _ptr(idx), _ptr(wts), _ptr(y), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_noalloc(d, x, rows, w_router, bias, weights, experts, shared, idx, wts, y, stream=None):
+    """moe_layer on the library's fixed per-GPU workspace (no allocation)."""
+    _check("moe_layer_noalloc", lib().moe_layer_noalloc(
+        ctypes.byref(d), _ptr(x), int(rows), _ptr(w_router), _ptr(bias), _ptr(weights),
+        _ptr(experts), _ptr(shared), _ptr(idx), _ptr(wts), _ptr(y), _stream(stream)))
 
 
 def moe_layer_profiled(d, x, rows, w_router, bias, weights, experts, shared, idx, wts, y, ws,

@@ -124,7 +124,7 @@ inline int shape_class(const moe_dims& d) {
   return 0;
 }
 
-inline TaggedLayout tagged_layout(const moe_dims& d) {
+constexpr TaggedLayout tagged_layout(const moe_dims& d) {
   TaggedLayout l{};
   const size_t pairs = static_cast<size_t>(kMaxRows) * d.top_k + kMaxRows;
   size_t o = 0;
@@ -134,6 +134,22 @@ inline TaggedLayout tagged_layout(const moe_dims& d) {
   l.ht = o;       o = align256(o + 8 * pairs * d.inter);
   l.part_t = o;   o = align256(o + 8 * pairs * d.hidden);
   l.end = o;
+  return l;
+}
+
+// The fused launch alone: the tagged area, then room for the routing outputs
+// when the caller passes no idx / wts (the fixed workspace of moe_layer_noalloc).
+struct FusedLayout {
+  TaggedLayout t;
+  size_t idx, wts, total;
+};
+constexpr FusedLayout fused_layout(const moe_dims& d) {
+  FusedLayout l{};
+  l.t = tagged_layout(d);
+  size_t o = l.t.end;
+  l.idx = o;      o = align256(o + 4 * static_cast<size_t>(kMaxRows) * kMaxK);
+  l.wts = o;      o = align256(o + 4 * static_cast<size_t>(kMaxRows) * kMaxK);
+  l.total = o;
   return l;
 }
 

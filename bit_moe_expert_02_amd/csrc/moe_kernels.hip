@@ -30,6 +30,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "../../include/moe.h"
@@ -1683,10 +1684,13 @@ struct Chain {
   uint16_t* x_next;
 };
 
+// fused_only: the workspace holds only the fused launch's area (the fixed
+// workspace of moe_layer_noalloc, lay::fused_layout), not a full decode layout.
 int run(const moe_dims* d, const void* x, int rows, const float* w_router, const float* bias,
         const void* weights, const moe_expert_ref* experts, const moe_expert_ref* shared,
         int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes, void* stream,
-        bool route, bool ffn, void* const* events, int n_events, const Chain* chain = nullptr) {
+        bool route, bool ffn, void* const* events, int n_events, const Chain* chain = nullptr,
+        bool fused_only = false) {
   int st = check_dims(d, rows);
   if (st) return st;
   if (rows == 0) return MOE_OK;
@@ -1694,8 +1698,17 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   if (route && !w_router) return MOE_EINVAL;
   if (ffn && (!weights || !experts || !y)) return MOE_EINVAL;
   if (!route && (!idx || !wts)) return MOE_EINVAL;
-  const lay::DecodeLayout l = lay::decode_layout(*d, rows);
-  if (ws_bytes < l.total) return MOE_EWORKSPACE;
+  lay::DecodeLayout l = lay::decode_layout(*d, rows);
+  if (fused_only) {
+    if (!(route && ffn)) return MOE_EINVAL;
+    const lay::FusedLayout f = lay::fused_layout(*d);
+    if (ws_bytes < f.total) return MOE_EWORKSPACE;
+    l = lay::DecodeLayout{};            // the split path's regions do not exist here
+    l.idx = f.idx;
+    l.wts = f.wts;
+  } else if (ws_bytes < l.total) {
+    return MOE_EWORKSPACE;
+  }
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   dev::Args a{};
   a.x = static_cast<const uint16_t*>(x);
@@ -1707,14 +1720,16 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   a.idx = idx ? idx : reinterpret_cast<int32_t*>(w8 + l.idx);
   a.wts = wts ? wts : reinterpret_cast<float*>(w8 + l.wts);
   a.y = y;
-  a.logits = reinterpret_cast<double*>(w8 + l.logits);
-  a.slots = reinterpret_cast<dev::SlotTable*>(w8 + l.slots);
-  a.order = reinterpret_cast<int32_t*>(w8 + l.order);
-  a.xinv = reinterpret_cast<float*>(w8 + l.xinv);
-  a.xrec = w8 + l.xrec;
-  a.xrow = l.xrow;
-  a.h = reinterpret_cast<float*>(w8 + l.h);
-  a.part = reinterpret_cast<float*>(w8 + l.part);
+  if (!fused_only) {
+    a.logits = reinterpret_cast<double*>(w8 + l.logits);
+    a.slots = reinterpret_cast<dev::SlotTable*>(w8 + l.slots);
+    a.order = reinterpret_cast<int32_t*>(w8 + l.order);
+    a.xinv = reinterpret_cast<float*>(w8 + l.xinv);
+    a.xrec = w8 + l.xrec;
+    a.xrow = l.xrow;
+    a.h = reinterpret_cast<float*>(w8 + l.h);
+    a.part = reinterpret_cast<float*>(w8 + l.part);
+  }
   a.R = rows;
   a.k = d->top_k;
   a.E = d->n_experts;
@@ -1736,6 +1751,36 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
     case 2: return launch_layer<dev::Shape<512, 256>>(d, rows, a, route, ffn, s, events, n_events);
     default: return MOE_ESHAPE;
   }
+}
+
+// ---------------------------------------------------------------------------
+// The fixed workspace of moe_layer_noalloc: one array per GPU, held until the
+// process ends, for callers that cannot allocate.  Host code never names the
+// array itself (that is a host-side stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and is kept per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t{4608} << 10;   // 4.5 MiB
+static_assert(lay::fused_layout(moe_dims{5120, 2304, lay::kMaxExperts, lay::kMaxK, 0}).total <= kScratchBytes,
+              "the fixed workspace holds the fused area of the largest supported layer");
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The device address of this device's scratch, looked up on the first call
+// on the device; null on failure.
+uint8_t* scratch_ptr() {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static uint8_t* ptrs[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    ptrs[dev] = static_cast<uint8_t*>(p);
+  }
+  return ptrs[dev];
 }
 
 template <class S>
@@ -1853,6 +1898,18 @@ int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const floa
               size_t ws_bytes, void* stream) {
   return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y,
                   ws, ws_bytes, stream, true, true, nullptr, 0);
+}
+
+int moe_layer_noalloc(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
+                      const float* sel_bias, const void* weights, const moe_expert_ref* experts,
+                      const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* stream) {
+  if (int st = moe::check_dims(dims, rows)) return st;
+  if (rows == 0) return MOE_OK;
+  if (moe::lay::fused_layout(*dims).total > moe::kScratchBytes) return MOE_EWORKSPACE;
+  uint8_t* ws = moe::scratch_ptr();
+  if (!ws) return MOE_EDEVICE;
+  return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y, ws,
+                  moe::kScratchBytes, stream, true, true, nullptr, 0, nullptr, true);
 }
 
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,

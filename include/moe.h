@@ -255,6 +255,26 @@ int moe_layer(const moe_dims* dims, const void* x_bf16, int32_t rows, const floa
               const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* ws,
               size_t ws_bytes, void* stream);
 
+/* moe_layer for callers that cannot allocate: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace argument: the fused launch's hand-off words live in a fixed
+ * device array of the library, 4.5 MiB per GPU (enough for rows <=
+ * MOE_MAX_DECODE_ROWS, top_k <= MOE_MAX_TOP_K and up to 512 experts at hidden
+ * 5120 / inter 2304), which each GPU the library runs on holds until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating
+ * library routine); its first call on a device looks up that device's array
+ * once.  Arguments, results and errors as moe_layer (idx / wts may be NULL);
+ * MOE_EWORKSPACE if the dims would need more than the array holds.
+ * Every call on a GPU shares that GPU's array, which keeps the last call's
+ * words: calls queued one after another (one stream) are correct, since each
+ * call's words carry its own tag; calls that overlap on one GPU (on
+ * different streams or from different threads without ordering) race and
+ * give wrong results.  A hand-off wait that gives up shows as NaN in y (the
+ * array's error word is not queryable). */
+int moe_layer_noalloc(const moe_dims* dims, const void* x_bf16, int32_t rows, const float* w_router,
+                      const float* sel_bias, const void* weights, const moe_expert_ref* experts,
+                      const moe_expert_ref* shared, int32_t* idx, float* wts, float* y, void* stream);
+
 /* moe_layer with timing: `events` holds n_events >= 2 hipEvent_t handles
  * created by the caller, recorded on the stream before and after the launch. */
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
