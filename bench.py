@@ -59,7 +59,8 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=1)
     p.add_argument("--workload", default="mixed_verify",
                    choices=["mixed_verify", "decode_q2", "fp4_layer", "draft128", "stack40_mixed",
-                            "fp4_stack20", "fp4_prefill", "verify_correlated", "policy_stack40"])
+                            "fp4_stack20", "fp4_prefill", "verify_correlated", "policy_stack40",
+                            "alloc_stack40"])
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="run one device copy of this many MiB first (a known-size reference "
                         "for hardware byte counters)")
@@ -666,6 +667,53 @@ def bench_policy(args, torch, L, LY, synth):
     print(json.dumps(line), flush=True)
 
 
+def bench_alloc(args, torch, L, LY, synth):
+    """The mixed stack with formats chosen per expert by moe_allocate_formats
+    (budget: the stack in Q2_0) from synthetic held-out errors, instead of the
+    seeded draw: the allocation's cost against all-Q2_0, its format shares, and
+    chained decode passes over the allocated stack."""
+    base = synth.WORKLOADS["stack40_mixed"]
+    err, tokens, energy = synth.alloc_inputs(base)
+    nb = [expert_bytes(base, f) for f in ("TERN160", "Q2_0", "Q3")]
+    t0 = time.perf_counter()
+    names, cost, nbytes = L.allocate_formats(err, tokens, energy, nb)
+    t_alloc = time.perf_counter() - t0
+    from oracle import alloc as OA
+    q2_cost = float(OA.costs(err, energy)[:, :, 1].sum())
+    budget = base.layers * base.n_experts * nb[1]
+    shares = {f: round(float((names == f).mean()), 4) for f in ("TERN160", "Q2_0", "Q3")}
+    say(f"allocation: cost {cost / q2_cost:.3f} of all-Q2_0, bytes {nbytes / budget:.5f} of budget, {shares}")
+    fmts = sorted(set(names.reshape(-1)))
+    pool = LY.make_pool(base, 0, fmts, args.pool)
+    layers = [LY.DeviceLayer(base, l, materialize=(), pool=pool, fmts=list(names[l])) for l in range(base.layers)]
+    torch.cuda.synchronize()
+    hev = HipEvents()
+    out_rows = {}
+    for rows in (1, 7):
+        noise = np.stack([synth.noise(base, l, rows) for l in range(base.layers)])
+        ms, b, u, _ = stack_passes(args, torch, L, LY, synth, hev, base, layers, rows,
+                                   lambda i: synth.x_bf16(base, 0, rows, 95_000 + i), noise)
+        gbps = b / (ms * 1e-3) / 1e9
+        out_rows[rows] = dict(ms_per_pass=round(ms, 4), tokens_per_s=round(rows / (ms * 1e-3), 2),
+                              pass_bytes=int(b), unique_experts_per_layer=round(u, 2), GBps=round(gbps, 1),
+                              frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
+        say(f"allocated stack rows {rows}: {ms:.3f} ms/pass, {gbps:.0f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        t1 = time.perf_counter()
+        OA.allocate(err, tokens, energy, nb)
+        t_oracle = time.perf_counter() - t1
+        cpu = dict(value=round(1.0 / t_oracle, 4), unit="allocations/s", cores=1, kind="oracle",
+                   sample=f"the oracle's allocation of the 40 x 384 stack, {t_oracle:.2f} s (library: {t_alloc:.3f} s)")
+    cfg = {"allocation": {"cost_vs_all_q2": round(cost / q2_cost, 4), "bytes": int(nbytes), "budget": int(budget),
+                          "shares": shares, "max_ternary_share_per_layer":
+                              round(float((names == "TERN160").mean(axis=1).max()), 4),
+                          "library_seconds": round(t_alloc, 3)}}
+    line = stack_line(args, base, out_rows, "alloc_stack40 chained decode tokens/s (per-expert allocated formats)",
+                      extra_cfg=cfg, cpu=cpu)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -695,6 +743,8 @@ def main():
         return bench_verify_correlated(args, torch, L, LY, synth)
     if args.workload == "policy_stack40":
         return bench_policy(args, torch, L, LY, synth)
+    if args.workload == "alloc_stack40":
+        return bench_alloc(args, torch, L, LY, synth)
     return main_decode(args, torch, L, LY, synth)
 
 

@@ -26,7 +26,8 @@ MAX_TOP_K = 8
 EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
            "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
-           "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status", "moe_layer_noalloc")
+           "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status", "moe_layer_noalloc",
+           "moe_allocate_formats")
 
 
 class MoeError(RuntimeError):
@@ -99,6 +100,9 @@ def lib():
         L.moe_stream_read.argtypes = [vp, sz, vp, i32, i32, vp]
         L.moe_workspace_status.restype = ctypes.c_int
         L.moe_workspace_status.argtypes = [vp, sz, vp]
+        L.moe_allocate_formats.restype = ctypes.c_int
+        L.moe_allocate_formats.argtypes = [i32, i32, vp, vp, vp, vp, ctypes.c_double, i32, i32, i32, vp,
+                                           vp, vp]
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
@@ -147,6 +151,26 @@ def unpack(fmt, buf, n, k, nthreads=0):
     _check("moe_unpack", lib().moe_unpack(FMT[fmt], buf.ctypes.data, buf.size, int(n), int(k),
                                           out.ctypes.data, int(nthreads)))
     return out
+
+
+def allocate_formats(err, tokens, energy, fmt_bytes, max_tern_frac=0.5, min_tokens=8, edge_first=2,
+                     edge_last=3):
+    """moe_allocate_formats: err [L, E, 3] (TERN160, Q2_0, Q3), tokens [L, E],
+    energy [L], fmt_bytes [3] -> (format names [L, E], total cost, total bytes)."""
+    err = np.ascontiguousarray(err, np.float64)
+    tokens = np.ascontiguousarray(tokens, np.int32)
+    energy = np.ascontiguousarray(energy, np.float64)
+    fb = np.ascontiguousarray(fmt_bytes, np.uint64)
+    L_, E_ = tokens.shape
+    out = np.empty((L_, E_), np.uint8)
+    cost = ctypes.c_double()
+    nbytes = ctypes.c_uint64()
+    _check("moe_allocate_formats", lib().moe_allocate_formats(
+        L_, E_, err.ctypes.data, tokens.ctypes.data, energy.ctypes.data, fb.ctypes.data,
+        float(max_tern_frac), int(min_tokens), int(edge_first), int(edge_last), out.ctypes.data,
+        ctypes.byref(cost), ctypes.byref(nbytes)))
+    names = np.vectorize(FMT_NAME.get)(out)
+    return names, cost.value, int(nbytes.value)
 
 
 # ----------------------------------------------------------------------------- device calls

@@ -52,11 +52,12 @@ class DeviceLayer:
     uint8 arrays; slot e takes pool[fmt][e % len(pool[fmt])].
     """
 
-    def __init__(self, wl, layer, materialize=(), pool=None, device="cuda", packed=None, flags=0):
+    def __init__(self, wl, layer, materialize=(), pool=None, device="cuda", packed=None, flags=0, fmts=None):
         import torch
         self.wl, self.layer = wl, layer
         self.dims = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k, flags)
-        self.fmts = synth.format_map(wl, layer)
+        # the routed experts' formats: the workload's seeded draw, or a given map
+        self.fmts = list(fmts) if fmts is not None else synth.format_map(wl, layer)
         table, shared, total = plan(self.fmts, wl.shared_fmt, wl.hidden, wl.inter)
         self.table, self.shared_table, self.total = table, shared, total
         st = L.check_experts(self.dims, table, total)

@@ -211,6 +211,42 @@ def zipf_routing(wl, layer, rows, s=1.1, stream=0):
     return idx.astype(np.int32), w.astype(np.float32)
 
 
+# Held-out relative output error of an expert per format: ternary, Q2_0, Q3
+# ([P1 §1], the GSQ quality proxy: 0.443 / 0.378 / 0.183).
+PAGE_ERRORS = (0.443, 0.378, 0.183)
+T_ALLOC = 7
+
+
+def alloc_inputs(wl, n_layers=None, heldout_tokens=61_440, s=1.1):
+    """Synthetic inputs of the per-expert format allocation of a stack:
+      err [L, E, 3]  PAGE_ERRORS per format x a per-(layer, expert) sensitivity
+                     LogNormal(0, 0.35) x a per-(layer, expert, format) factor
+                     LogNormal(0, 0.15) x a per-layer factor LogNormal(0, 0.3)
+                     (layer 32 of 40 x3: the pages' most sensitive layer);
+      tokens [L, E]  held-out tokens per expert: heldout_tokens x top_k pairs
+                     per layer over Zipf(s) expert popularity (a seeded
+                     permutation per layer);
+      energy [L]     the layer's routed output energy, LogNormal(0, 0.5)."""
+    L = n_layers or wl.layers
+    E = wl.n_experts
+    g = rng(wl, 0, T_ALLOC)
+    base = np.asarray(PAGE_ERRORS)
+    layer_f = g.lognormal(0.0, 0.3, L)
+    if L > 32:
+        layer_f[32] *= 3.0
+    sens = g.lognormal(0.0, 0.35, (L, E))
+    per_f = g.lognormal(0.0, 0.15, (L, E, 3))
+    err = base[None, None, :] * sens[:, :, None] * per_f * layer_f[:, None, None]
+    tokens = np.empty((L, E), np.int32)
+    ranks = -s * np.log(np.arange(1, E + 1, dtype=np.float64))
+    for l in range(L):
+        p = np.empty(E)
+        p[g.permutation(E)] = np.exp(ranks)
+        tokens[l] = g.multinomial(heldout_tokens * wl.top_k, p / p.sum())
+    energy = g.lognormal(0.0, 0.5, L)
+    return err, tokens, energy
+
+
 def noise(wl, layer, rows):
     """N(0,1) fp32 [rows x H] added to a layer's output before it feeds the next layer."""
     return rng(wl, layer, T_NOISE).standard_normal((rows, wl.hidden), dtype=np.float32)

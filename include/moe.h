@@ -129,6 +129,33 @@ int moe_pack(int fmt, const float* w, int64_t n, int64_t k, void* dst, size_t ds
 int moe_unpack(int fmt, const void* src, size_t src_bytes, int64_t n, int64_t k, float* w,
                int nthreads);
 
+/* Per-expert format allocation for a stack of n_layers x n_experts routed
+ * experts ("[Strata] DeepSeek V4.1 Flash on a single 4090", section 5.1):
+ * each expert gets TERN160, Q2_0 or Q3 so that the stack's bytes stay within
+ * those of the whole stack in Q2_0, by a Lagrangian relaxation (bisection on
+ * the multiplier) and a greedy fill of the bytes left over.
+ *   err        [n_layers x n_experts x 3] host: held-out output error of the
+ *              expert in TERN160, Q2_0, Q3 (>= 0)
+ *   tokens     [n_layers x n_experts] host: held-out tokens routed to it
+ *   energy     [n_layers] host: the layer's routed output energy (> 0)
+ *   fmt_bytes  [3] host: bytes of one expert in TERN160, Q2_0, Q3 (increasing)
+ *   cost = err / energy, doubled on the first edge_first and last edge_last
+ *   layers; at most floor(max_tern_frac * n_experts) ternary experts per
+ *   layer; experts with fewer than min_tokens tokens stay Q2_0 (the pages:
+ *   0.5, 8, 2, 3).  Per expert the multiplier picks the least cost + lam *
+ *   bytes (equal values: Q2_0, then ternary, then Q3); over the cap, the
+ *   ternary experts whose best other value is closest go back (equal: the
+ *   higher id first); the greedy fill takes upgrades to a larger, cheaper
+ *   format by cost saved per extra byte (equal: lower expert, lower format).
+ *   fmt_out    [n_layers x n_experts] host, out: moe_format tags
+ *   cost_out, bytes_out: the allocation's total cost and bytes (or NULL)
+ * Host only, deterministic.  MOE_EINVAL on a null pointer, a size <= 0, a
+ * negative or non-finite error, a non-positive energy or unordered sizes. */
+int moe_allocate_formats(int32_t n_layers, int32_t n_experts, const double* err, const int32_t* tokens,
+                         const double* energy, const uint64_t* fmt_bytes, double max_tern_frac,
+                         int32_t min_tokens, int32_t edge_first, int32_t edge_last, uint8_t* fmt_out,
+                         double* cost_out, uint64_t* bytes_out);
+
 /* ------------------------------------------------------------------------ */
 /* Device layer.                                                             */
 /* ------------------------------------------------------------------------ */

@@ -184,6 +184,39 @@ void workspaces() {
   check(moe_workspace_bytes(&d, 55) >= tagged_layout(d).end, "many-row workspace holds the tagged area");
 }
 
+void allocator() {
+  // a random 5-layer, 40-expert instance: guardrails hold, bytes within budget
+  const int L = 5, E = 40;
+  std::mt19937 rng(3);
+  std::uniform_real_distribution<double> u(0.05, 1.0);
+  std::vector<double> err(static_cast<size_t>(L) * E * 3), energy(L);
+  std::vector<int32_t> tokens(static_cast<size_t>(L) * E);
+  for (double& v : err) v = u(rng);
+  for (double& v : energy) v = u(rng);
+  for (size_t i = 0; i < tokens.size(); ++i) tokens[i] = static_cast<int32_t>(i % 50);
+  const uint64_t fb[3] = {7624704, 9953280, 15206400};
+  std::vector<uint8_t> fmt(static_cast<size_t>(L) * E);
+  double cost = 0.0;
+  uint64_t bytes = 0;
+  check(moe_allocate_formats(L, E, err.data(), tokens.data(), energy.data(), fb, 0.5, 8, 2, 3, fmt.data(), &cost,
+                             &bytes) == MOE_OK, "allocate");
+  check(bytes <= static_cast<uint64_t>(L) * E * fb[1], "allocation within budget");
+  for (int l = 0; l < L; ++l) {
+    int tern = 0;
+    for (int e = 0; e < E; ++e) {
+      const uint8_t f = fmt[static_cast<size_t>(l) * E + e];
+      tern += f == MOE_FMT_TERN160;
+      if (tokens[static_cast<size_t>(l) * E + e] < 8) check(f == MOE_FMT_Q2_0, "locked expert stays Q2_0");
+    }
+    check(tern <= E / 2, "ternary cap");
+  }
+  const uint64_t bad[3] = {fb[1], fb[0], fb[2]};
+  check(moe_allocate_formats(L, E, err.data(), tokens.data(), energy.data(), bad, 0.5, 8, 2, 3, fmt.data(),
+                             nullptr, nullptr) == MOE_EINVAL, "unordered sizes");
+  check(moe_allocate_formats(0, E, err.data(), tokens.data(), energy.data(), fb, 0.5, 8, 2, 3, fmt.data(),
+                             nullptr, nullptr) == MOE_EINVAL, "no layers");
+}
+
 void dims_checks() {
   const moe_dims good{5120, 2304, 384, 6, 0};
   check(moe::check_dims(&good, 8) == MOE_OK, "8 rows");
@@ -210,6 +243,7 @@ int main() {
   expert_tables();
   workspaces();
   dims_checks();
+  allocator();
   if (failures) {
     std::fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;
