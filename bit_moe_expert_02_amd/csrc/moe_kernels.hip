@@ -788,6 +788,97 @@ __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, 
   }
 }
 
+// The same table, built by wave 0 of a fused-launch worker straight from the
+// published selection words (entry m: kSelWords words at ew + kSelWords * m,
+// as the selection writes them).  Lane m holds pair m; which pairs repeat an
+// expert, the rank of each distinct expert and the tile offsets before it
+// come from cross-lane reads of registers, so the only LDS traffic is one
+// read of the lane's entry and the table's stores: this runs between the
+// selection and the first weight load of every worker.
+template <class S>
+__device__ __forceinline__ void slot_table_from_words(const Args& a, const uint32_t* ew, const moe_expert_ref& shref,
+                                                      SlotTable* tab) {
+  const int lane = tid();
+  const int n = a.R * a.k;
+  const bool act = lane < n;
+  // the entry's words: id | fmt << 16, weight bits, then the 32-bit halves
+  // of its gate, up and down offsets
+  uint32_t q[kSelWords];
+#pragma unroll
+  for (int f = 0; f < kSelWords; ++f) q[f] = act ? ew[kSelWords * lane + f] : 0u;
+  const int id = static_cast<int>(q[0] & 0xFFFFu);
+  const uint32_t fmt = q[0] >> 16;
+  // pairs of the same expert before this one (its position in the slot's
+  // rows) and in all (the slot's row count); the loop is uniform over lanes
+  int before = 0, same = 0;
+  for (int j = 0; j < n; ++j) {
+    const bool eq = __builtin_amdgcn_readlane(id, j) == id;
+    same += eq ? 1 : 0;
+    before += (eq && j < lane) ? 1 : 0;
+  }
+  const bool first = act && before == 0;
+  const uint64_t firsts = __ballot(first);
+  const int tg = first ? tiles_of<S, true>(fmt) : 0;
+  const int td = first ? tiles_of<S, false>(fmt) : 0;
+  // slot = number of distinct experts of lower id; its first items follow
+  // the tiles of those experts
+  int rank = 0, og = 0, od = 0, tot_g = 0, tot_d = 0;
+  for (uint64_t m = firsts; m != 0; m &= m - 1) {
+    const int j = __builtin_ctzll(m);
+    const int gj = __builtin_amdgcn_readlane(tg, j), dj = __builtin_amdgcn_readlane(td, j);
+    const bool lt = __builtin_amdgcn_readlane(id, j) < id;
+    rank += lt ? 1 : 0;
+    og += lt ? gj : 0;
+    od += lt ? dj : 0;
+    tot_g += gj;
+    tot_d += dj;
+  }
+  const int n_active = __popcll(firsts);
+  if (act && before < kMaxRows) {   // a lost selection names one expert n times: keep the first kMaxRows
+    SlotEntry& e = tab->e[rank];
+    e.row[before] = lane / a.k;
+    e.pair[before] = lane;
+    e.w[before] = __builtin_bit_cast(float, q[1]);
+    if (first) {
+      e.ref.fmt = fmt;
+      e.ref.reserved = 0;
+      e.ref.gate = (static_cast<uint64_t>(q[3]) << 32) | q[2];
+      e.ref.up = (static_cast<uint64_t>(q[5]) << 32) | q[4];
+      e.ref.down = (static_cast<uint64_t>(q[7]) << 32) | q[6];
+      e.expert = id;
+      e.nt = same < kMaxRows ? same : kMaxRows;
+      tab->gu_off[rank] = og;
+      tab->dn_off[rank] = od;
+    }
+  }
+  if (a.shared && lane < a.R) {
+    SlotEntry& e = tab->e[n_active];
+    e.row[lane] = lane;
+    e.pair[lane] = n + lane;
+    e.w[lane] = 1.0f;
+  }
+  if (lane == 0) {
+    int ng = tot_g, nd = tot_d;
+    if (a.shared) {
+      SlotEntry& e = tab->e[n_active];
+      e.ref = shref;
+      e.expert = -1;
+      e.nt = a.R;
+      tab->gu_off[n_active] = ng;
+      tab->dn_off[n_active] = nd;
+      ng += a.shared_early ? 0 : tiles_of<S, true>(shref.fmt);
+      nd += tiles_of<S, false>(shref.fmt);
+    }
+    const int ns = n_active + (a.shared ? 1 : 0);
+    tab->gu_off[ns] = ng;
+    tab->dn_off[ns] = nd;
+    tab->n_active = n_active;
+    tab->n_slots = ns;
+    tab->n_gu = ng;
+    tab->n_dn = nd;
+  }
+}
+
 // Activation records of every format for every row, built by kPrepWGs
 // workgroups (p = 0 .. kPrepWGs-1).
 template <class S, class F>
@@ -1141,6 +1232,23 @@ __device__ __forceinline__ void run_item(const Args& a, const SlotTable* tab, co
   __syncthreads();
 }
 
+// One work item of the fused launch: the table is in this workgroup's LDS
+// for the whole call, so the slot's entry is used in place.  The slot is the
+// number of slot starts at or below the item, counted with ballots over one
+// LDS read per lane (at most kMaxSlots + 1 slots).
+template <class S, int STAGE>
+__device__ __forceinline__ void run_item_fused(const Args& a, const SlotTable& tab, const int* offs, int ns, int item,
+                                               uint8_t* lds, uint32_t tag) {
+  static_assert(kMaxSlots + 1 <= 128, "two offsets a lane");
+  const int lane = tid() & 63;
+  const int o0 = lane < ns ? offs[lane] : 0x7fffffff;
+  const int o1 = lane + 64 < ns ? offs[lane + 64] : 0x7fffffff;
+  const int slot = __popcll(__ballot(o0 <= item)) + __popcll(__ballot(o1 <= item)) - 1;
+  const int start = slot < 64 ? __builtin_amdgcn_readlane(o0, slot) : __builtin_amdgcn_readlane(o1, slot - 64);
+  run_slot<S, STAGE, true>(a, tab.e[slot], item - start, lds, tag);
+  __syncthreads();
+}
+
 // Work items of one list, strided over `nw` workers (this is worker w).
 // STAGE as in run_slot; the list is the down list for STAGE 0, else the
 // gate/up list.
@@ -1275,7 +1383,6 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   __shared__ SlotTable tab;
   __shared__ moe_expert_ref shref;
   __shared__ SlotEntry sl;
-  __shared__ int offs[2][kMaxSlots + 2];
   if (tid() == 0 && a.shared) shref = *a.shared;
   stage_x_row<S>(a, 0, lds);   // before any wait: every gate/up item of row 0 finds x here
 
@@ -1311,9 +1418,6 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   // the selection of every row, then the slot table in LDS; the selection's
   // staging shares the dynamic region with the tiles' records
   uint32_t* ew = reinterpret_cast<uint32_t*>(lds + S::LDS_SEL_OFF);
-  moe_expert_ref* eref = reinterpret_cast<moe_expert_ref*>(lds + S::LDS_SEL_OFF + S::LDS_SEL_WORDS);
-  int* ids = reinterpret_cast<int*>(eref + kMaxRows * kMaxK);
-  float* wv = reinterpret_cast<float*>(ids + kMaxRows * kMaxK);
   const int n = a.R * a.k;
   // One wave polls the whole selection, a few words a lane: a thousand
   // workgroups polling with every lane would hammer the same lines, and a
@@ -1343,28 +1447,14 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
         ew[i] = f == 0 ? e0[0] << 16 : f == 1 ? 0x7FC00000u : e0[f];
       }
     }
+    // the words just stored are read back by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    slot_table_from_words<S>(a, ew, shref, &tab);
   }
-  __syncthreads();
-  if (tid() < n) {
-    const uint32_t* e = ew + tid() * kSelWords;
-    ids[tid()] = static_cast<int>(e[0] & 0xFFFFu);
-    wv[tid()] = __builtin_bit_cast(float, e[1]);
-    moe_expert_ref& f = eref[tid()];
-    f.fmt = e[0] >> 16;
-    f.reserved = 0;
-    f.gate = (static_cast<uint64_t>(e[3]) << 32) | e[2];
-    f.up = (static_cast<uint64_t>(e[5]) << 32) | e[4];
-    f.down = (static_cast<uint64_t>(e[7]) << 32) | e[6];
-  }
-  __syncthreads();
-  if (tid() < 64) build_slot_table<S>(a, ids, wv, &tab, false, eref, &shref);
   __syncthreads();
   const int ns = uniform(tab.n_slots);
-  for (int q = tid(); q <= ns; q += kThreads) {
-    offs[0][q] = tab.gu_off[q];
-    offs[1][q] = tab.dn_off[q];
-  }
-  __syncthreads();
   const int n_gu = uniform(tab.n_gu), n_dn = uniform(tab.n_dn);
   // the down list is taken from the shared expert's tiles on (they are the
   // list's last, from n_dn - sh_dn): its h is ready long before the routed
@@ -1375,8 +1465,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   // get its later positions, so the routed gate/up items start on free
   // workers as soon as the selection is out
   for (int j = (w - nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
-    if (j < n_gu) run_item<S, 2, true>(a, &tab, offs[0], ns, j, sl, lds, tag);
-    else run_item<S, 0, true>(a, &tab, offs[1], ns, (j - n_gu + n_dn - sh_dn) % n_dn, sl, lds, tag);
+    if (j < n_gu) run_item_fused<S, 2>(a, tab, tab.gu_off, ns, j, lds, tag);
+    else run_item_fused<S, 0>(a, tab, tab.dn_off, ns, (j - n_gu + n_dn - sh_dn) % n_dn, lds, tag);
   }
 }
 
