@@ -932,25 +932,34 @@ __device__ __forceinline__ void router_wg(const Args& a, int e, double* red, uin
     const int j = tid() + i * kThreads;
     w[i] = j < H / 4 ? wr[j] : float4{0.f, 0.f, 0.f, 0.f};
   }
+  // the x rows of a group are all requested before any is used: one round
+  // trip per group of kXG rows, not one per row
+  constexpr int kXG = 4;
 #pragma unroll
-  for (int r = 0; r < kMaxRows; ++r) {
-    if (r < a.R) {
-      uint2 xb[CH];
+  for (int r0 = 0; r0 < kMaxRows; r0 += kXG) {
+    if (r0 < a.R) {
+      uint2 xb[kXG][CH];
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        const int j = tid() + i * kThreads;
-        xb[i] = j < H / 4 ? *reinterpret_cast<const uint2*>(a.x + static_cast<size_t>(r) * H + 4 * j)
-                          : uint2{0u, 0u};
+      for (int g = 0; g < kXG; ++g)
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const int j = tid() + i * kThreads;
+          xb[g][i] = (r0 + g < a.R && j < H / 4)
+                         ? *reinterpret_cast<const uint2*>(a.x + static_cast<size_t>(r0 + g) * H + 4 * j)
+                         : uint2{0u, 0u};
+        }
+#pragma unroll
+      for (int g = 0; g < kXG; ++g) {
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          s = fma(static_cast<double>(w[i].x), static_cast<double>(bf16_bits_to_f32(xb[g][i].x & 0xFFFFu)), s);
+          s = fma(static_cast<double>(w[i].y), static_cast<double>(bf16_bits_to_f32(xb[g][i].x >> 16)), s);
+          s = fma(static_cast<double>(w[i].z), static_cast<double>(bf16_bits_to_f32(xb[g][i].y & 0xFFFFu)), s);
+          s = fma(static_cast<double>(w[i].w), static_cast<double>(bf16_bits_to_f32(xb[g][i].y >> 16)), s);
+        }
+        acc[r0 + g] = s;
       }
-      double s = 0.0;
-#pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        s = fma(static_cast<double>(w[i].x), static_cast<double>(bf16_bits_to_f32(xb[i].x & 0xFFFFu)), s);
-        s = fma(static_cast<double>(w[i].y), static_cast<double>(bf16_bits_to_f32(xb[i].x >> 16)), s);
-        s = fma(static_cast<double>(w[i].z), static_cast<double>(bf16_bits_to_f32(xb[i].y & 0xFFFFu)), s);
-        s = fma(static_cast<double>(w[i].w), static_cast<double>(bf16_bits_to_f32(xb[i].y >> 16)), s);
-      }
-      acc[r] = s;
     }
   }
   const int wave = tid() >> 6, lane = tid() & 63, nw = kThreads / 64;
@@ -1451,7 +1460,11 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // every wave of this workgroup waits for the table, and the waves it
+    // shares its SIMD with are decoding: it goes first meanwhile
+    __builtin_amdgcn_s_setprio(3);
     slot_table_from_words<S>(a, ew, shref, &tab);
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
   const int ns = uniform(tab.n_slots);
