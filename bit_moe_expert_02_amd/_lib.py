@@ -27,7 +27,8 @@ EXPORTS = ("moe_status_string", "moe_packed_bytes", "moe_pack", "moe_unpack",
            "moe_workspace_bytes", "moe_check_experts", "moe_route", "moe_expert_ffn",
            "moe_layer", "moe_layer_profiled", "moe_stack_decode", "moe_quant_mxfp8",
            "moe_stream_read", "moe_set_spin_limit", "moe_workspace_status", "moe_layer_noalloc",
-           "moe_allocate_formats")
+           "moe_allocate_formats", "moe_cache_create", "moe_cache_destroy", "moe_cache_plan",
+           "moe_copy_share", "moe_cpu_expert_ffn", "moe_add_chain")
 
 
 class MoeError(RuntimeError):
@@ -106,6 +107,18 @@ def lib():
         L.moe_stack_decode.restype = ctypes.c_int
         L.moe_stack_decode.argtypes = [dims_p, i32, ctypes.POINTER(LayerWeights), i32, vp, vp, vp,
                                        vp, vp, vp, sz, vp]
+        L.moe_cache_create.restype = ctypes.c_int
+        L.moe_cache_create.argtypes = [i32, i32, i32, ctypes.POINTER(vp)]
+        L.moe_cache_destroy.restype = None
+        L.moe_cache_destroy.argtypes = [vp]
+        L.moe_cache_plan.restype = ctypes.c_int
+        L.moe_cache_plan.argtypes = [vp, i32, i32, i32, vp, ctypes.c_double, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_copy_share.restype = ctypes.c_double
+        L.moe_copy_share.argtypes = [ctypes.c_double, ctypes.c_double]
+        L.moe_cpu_expert_ffn.restype = ctypes.c_int
+        L.moe_cpu_expert_ffn.argtypes = [dims_p, i32, vp, vp, vp, vp, i32, vp, vp, vp, i32]
+        L.moe_add_chain.restype = ctypes.c_int
+        L.moe_add_chain.argtypes = [vp, vp, vp, vp, sz, vp]
         _lib = L
     return _lib
 
@@ -276,3 +289,66 @@ def moe_set_spin_limit(polls):
     if prev < 0:
         raise MoeError("moe_set_spin_limit", prev)
     return prev
+
+
+# ----------------------------------------------------------------------------- stacks larger than HBM
+class SlotCache:
+    """moe_cache_create / moe_cache_plan / moe_cache_destroy (host only)."""
+
+    def __init__(self, n_layers, n_experts, n_slots):
+        h = ctypes.c_void_p()
+        _check("moe_cache_create", lib().moe_cache_create(int(n_layers), int(n_experts), int(n_slots),
+                                                          ctypes.byref(h)))
+        self.h, self.n_experts, self.n_slots = h, int(n_experts), int(n_slots)
+
+    def plan(self, layer, idx, copy_share):
+        """idx: host int32 [rows, top_k] -> dict(slot_of [E], copies [(expert, slot)],
+        cpu [experts], idx_gpu [rows, top_k])."""
+        idx = np.ascontiguousarray(idx, np.int32)
+        rows, k = idx.shape
+        n = rows * k
+        slot_of = np.empty(self.n_experts, np.int32)
+        ce, cs, cpu, idx_gpu = (np.empty(max(n, 1), np.int32) for _ in range(4))
+        nc, nu = ctypes.c_int32(), ctypes.c_int32()
+        _check("moe_cache_plan", lib().moe_cache_plan(
+            self.h, int(layer), rows, k, idx.ctypes.data, float(copy_share), slot_of.ctypes.data,
+            ce.ctypes.data, cs.ctypes.data, ctypes.byref(nc), cpu.ctypes.data, ctypes.byref(nu),
+            idx_gpu.ctypes.data))
+        return {"slot_of": slot_of,
+                "copies": [(int(ce[i]), int(cs[i])) for i in range(nc.value)],
+                "cpu": [int(cpu[i]) for i in range(nu.value)],
+                "idx_gpu": idx_gpu[:n].reshape(rows, k).copy()}
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def copy_share(pcie_bytes_per_s, cpu_bytes_per_s):
+    return float(lib().moe_copy_share(float(pcie_bytes_per_s), float(cpu_bytes_per_s)))
+
+
+def cpu_expert_ffn(d, fmt, gate, up, down, x_bf16, row_ids, row_w, y, nthreads=0):
+    """moe_cpu_expert_ffn on host numpy arrays: y [rows, H] fp32 accumulates
+    row_w[j] * FFN(x[row_ids[j]])."""
+    for a in (gate, up, down, x_bf16, y):
+        assert a.flags.c_contiguous
+    assert y.dtype == np.float32
+    rid = np.ascontiguousarray(row_ids, np.int32)
+    rw = np.ascontiguousarray(row_w, np.float32)
+    _check("moe_cpu_expert_ffn", lib().moe_cpu_expert_ffn(
+        ctypes.byref(d), FMT[fmt] if isinstance(fmt, str) else int(fmt), gate.ctypes.data,
+        up.ctypes.data, down.ctypes.data, x_bf16.ctypes.data, len(rid), rid.ctypes.data,
+        rw.ctypes.data, y.ctypes.data, int(nthreads)))
+
+
+def moe_add_chain(y, add, noise, x_next, stream=None):
+    _check("moe_add_chain", lib().moe_add_chain(_ptr(y), _ptr(add), _ptr(noise), _ptr(x_next),
+                                                y.numel(), _stream(stream)))

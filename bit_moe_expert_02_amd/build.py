@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 
-SOURCES = ["moe_kernels.hip", "prefill.hip", "pack.cpp", "host_api.cpp", "alloc.cpp"]
+SOURCES = ["moe_kernels.hip", "prefill.hip", "pack.cpp", "host_api.cpp", "alloc.cpp", "offload.cpp"]
 HEADERS = ["dev_common.h", "formats_dev.h", "host_api.h", "host_common.h", "layout.h", "prefill.h"]
 
 HIPCC_FLAGS = [

@@ -717,8 +717,12 @@ __device__ __forceinline__ void build_slot_table(const Args& a, const int* ids, 
   __shared__ int tg[kMaxSlots + 1], td[kMaxSlots + 1];
   const int lane = tid();
   const int n = a.R * a.k;
-  const int v = lane < n ? ids[lane] : 0x7fffffff;
-  bool first = lane < n;
+  // an id outside [0, E) names no expert: -1 is a pair the caller computes
+  // elsewhere, anything else is invalid (the combine makes that row NaN);
+  // neither reads the expert table
+  const bool live = lane < n && ids[lane] >= 0 && ids[lane] < a.E;
+  const int v = live ? ids[lane] : 0x7fffffff;
+  bool first = live;
   int rank = 0;
   for (int m = 0; m < n; ++m) {
     const int vm = ids[m];
@@ -1491,10 +1495,36 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   if (i >= a.R * S::kH) return;
   const int r = i / S::kH, n = i - r * S::kH;
   float s = 0.0f;
-  for (int j = 0; j < a.k; ++j)
-    s += a.part[static_cast<size_t>(r * a.k + a.order[r * a.k + j]) * S::kH + n];
+  bool bad = false;
+  for (int j = 0; j < a.k; ++j) {
+    const int q = a.order[r * a.k + j];
+    const int e = a.idx[r * a.k + q];
+    if (e == -1) continue;   // computed by the caller elsewhere: contributes nothing here
+    bad = bad || e < -1 || e >= a.E;
+    if (e >= 0 && e < a.E) s += a.part[static_cast<size_t>(r * a.k + q) * S::kH + n];
+  }
   if (a.shared) s += a.part[static_cast<size_t>(a.R * a.k + r) * S::kH + n];
-  a.y[i] = s;
+  a.y[i] = bad ? __builtin_nanf("") : s;
+}
+
+// y += add (when given), then, when x_next is given, x_next = bf16 (round to
+// nearest even) of y + noise: the end of a layer step whose outputs were
+// computed in parts.
+__global__ __launch_bounds__(kThreads) void k_add_chain(float* y, const float* add, const float* noise,
+                                                        uint16_t* x_next, size_t n) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + tid();
+  if (i >= n) return;
+  float s = y[i];
+  if (add) {
+    s += add[i];
+    y[i] = s;
+  }
+  if (x_next) {
+    const float v = noise ? s + noise[i] : s;
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
+    x_next[i] = static_cast<uint16_t>(u >> 16);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1965,6 +1995,16 @@ int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
     case 8: hipLaunchKernelGGL(moe::dev::k_stream_read<8>, g, b, 0, s, p, n16, sink); break;
     default: return MOE_EINVAL;
   }
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
+}
+
+int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, size_t n, void* stream) {
+  if (!y) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  const size_t blocks = (n + moe::dev::kThreads - 1) / moe::dev::kThreads;
+  if (blocks > 0x7fffffffu) return MOE_EINVAL;
+  hipLaunchKernelGGL(moe::dev::k_add_chain, dim3(static_cast<unsigned>(blocks)), dim3(moe::dev::kThreads), 0,
+                     static_cast<hipStream_t>(stream), y, add, noise, static_cast<uint16_t*>(x_next), n);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 

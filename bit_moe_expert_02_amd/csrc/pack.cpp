@@ -255,8 +255,11 @@ void pack_rows(int fmt, const float* w, int64_t n, int64_t k, uint8_t* dst, int6
 // --------------------------------------------------------------- unpack
 const float kE2M1[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
-bool unpack_rows(int fmt, const uint8_t* src, int64_t n, int64_t k, float* w, int64_t r0,
-                 int64_t r1) {
+}  // namespace
+
+// Rows [r0, r1) of a packed [n x k] matrix decoded to fp32 (exact), row r at
+// out + (r - r0) * k.  False if a code is invalid.
+bool unpack_rows(int fmt, const uint8_t* src, int64_t n, int64_t k, float* out, int64_t r0, int64_t r1) {
   const FormatInfo fi = format_info(fmt);
   const int64_t nb = blocks_per_row(fmt, k);
   const uint8_t* codes = src;
@@ -320,13 +323,12 @@ bool unpack_rows(int fmt, const uint8_t* src, int64_t n, int64_t k, float* w, in
       }
       const int64_t start = b * fi.block;
       const int64_t cnt = std::min<int64_t>(fi.block, k - start);
-      std::memcpy(w + r * k + start, v, static_cast<size_t>(cnt) * sizeof(float));
+      std::memcpy(out + (r - r0) * k + start, v, static_cast<size_t>(cnt) * sizeof(float));
     }
   }
   return true;
 }
 
-}  // namespace
 }  // namespace moe
 
 extern "C" size_t moe_packed_bytes(int fmt, int64_t n, int64_t k) {
@@ -363,7 +365,7 @@ extern "C" int moe_unpack(int fmt, const void* src, size_t src_bytes, int64_t n,
     if (a >= b) continue;
     pool.emplace_back([&, i, a, b] {
       status[static_cast<size_t>(i)] =
-          moe::unpack_rows(fmt, static_cast<const uint8_t*>(src), n, k, w, a, b) ? 1 : 0;
+          moe::unpack_rows(fmt, static_cast<const uint8_t*>(src), n, k, w + a * k, a, b) ? 1 : 0;
     });
   }
   for (auto& th : pool) th.join();

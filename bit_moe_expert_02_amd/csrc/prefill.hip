@@ -623,8 +623,10 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
 #pragma unroll
   for (int q = 0; q < MOE_MAX_TOP_K; ++q) {
     id[q] = q < a.k ? a.idx[r * a.k + q] : 0x7fffffff;
-    bad = bad || (q < a.k && (id[q] < 0 || id[q] >= a.E));
-    v[q] = q < a.k ? a.part[static_cast<size_t>(r * a.k + q) * H + n] : 0.0f;
+    // -1: a pair the caller computes elsewhere (no list entry, adds 0); any
+    // other id outside [0, E) is invalid and makes the row NaN
+    bad = bad || (q < a.k && (id[q] < -1 || id[q] >= a.E));
+    v[q] = (q < a.k && id[q] >= 0) ? a.part[static_cast<size_t>(r * a.k + q) * H + n] : 0.0f;
   }
 #pragma unroll
   for (int q = 0; q < MOE_MAX_TOP_K; ++q) {

@@ -237,6 +237,9 @@ int moe_quant_mxfp8(const void* x_bf16, int32_t rows, int32_t k, void* codes, vo
  *   shared     [1] moe_expert_ref, device, or NULL (no shared expert)
  *   y          [rows x H] fp32, device, out (overwritten)
  * Deterministic: the same inputs give bitwise the same y.
+ * An idx entry of -1 is a pair the caller computes elsewhere (an expert the
+ * CPU serves, moe_cache_plan): it adds nothing to y and its expert entry is
+ * not read.  Any other id outside [0, n_experts) makes its row of y NaN.
  * rows <= MOE_MAX_DECODE_ROWS: the decode path, any formats.
  * MOE_MAX_DECODE_ROWS < rows <= MOE_MAX_PREFILL_ROWS: the many-row path
  * ("[Strata] DeepSeek V4.1 Flash on a single 4090", section 4: prefill runs
@@ -382,6 +385,74 @@ int32_t moe_set_spin_limit(int32_t polls);
  * fails. */
 int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid, int32_t unroll,
                     void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stacks larger than HBM.
+ * "DeepSeek-V4.1-Flash served three ways on 4xL20", section 3C: one engine
+ * keeps every expert in a pinned host store and only a slot cache on the
+ * device; a layer's missing experts are either copied to the device or
+ * computed on the CPU, the number copied set by the ratio of the two
+ * channels' measured bandwidths (section 5: f / (1 - f) = effective PCIe rate
+ * / effective CPU rate; "Model task radar 2026-11-03: when the accelerator
+ * flips", section 6: q* ~ m * B_P / B_H to first order).  "[Strata] DeepSeek V4.1 Flash on a single 4090",
+ * section 5.2: a device LRU of experts in front of a pinned host arena.
+ *
+ * The calls below are host code; the caller moves the bytes (pinned host ->
+ * device slots) and runs the device part with moe_route / moe_expert_ffn
+ * (pairs the CPU serves marked -1) and moe_add_chain.
+ * ------------------------------------------------------------------------ */
+typedef struct moe_slot_cache moe_slot_cache;
+
+/* A cache of n_slots device expert slots for a stack of n_layers x
+ * n_experts routed experts, all slots empty.  Host memory only (the slots'
+ * device memory is the caller's).  *out is NULL on error (MOE_EINVAL). */
+int moe_cache_create(int32_t n_layers, int32_t n_experts, int32_t n_slots, moe_slot_cache** out);
+void moe_cache_destroy(moe_slot_cache* cache);
+
+/* One layer step: which of the experts that idx selects are in a slot (hits),
+ * which are copied into a slot now, and which the CPU computes.
+ *   idx         host [rows x top_k], every id in [0, n_experts)
+ *   copy_share  0 .. 1: the share of the step's misses to copy (rounded to
+ *               the nearest count, halves up); moe_copy_share gives it from
+ *               measured bandwidths
+ * Misses are copied in order of most pairs, then lower id.  A copy takes a
+ * free slot (lowest index), else the least recently used slot (lowest index
+ * on ties) that this step's experts do not use; when none is left the miss
+ * goes to the CPU.  Outputs (host arrays the caller provides):
+ *   slot_of     [n_experts]  the slot of each expert of `layer` after the
+ *               step (-1: not resident); the slots of this step's device
+ *               experts hold them once the copies below are done
+ *   copy_expert, copy_slot [rows x top_k]  the copies, *n_copy of them
+ *   cpu_expert  [rows x top_k]  the experts the CPU serves, ascending, *n_cpu
+ *   idx_gpu     [rows x top_k]  idx with the CPU's experts replaced by -1
+ * MOE_EINVAL on a null pointer, an id out of range or a share outside [0, 1]
+ * (the cache is then unchanged). */
+int moe_cache_plan(moe_slot_cache* cache, int32_t layer, int32_t rows, int32_t top_k, const int32_t* idx,
+                   double copy_share, int32_t* slot_of, int32_t* copy_expert, int32_t* copy_slot,
+                   int32_t* n_copy, int32_t* cpu_expert, int32_t* n_cpu, int32_t* idx_gpu);
+
+/* The share of misses to copy when copies run at pcie_bytes_per_s and the
+ * CPU computes experts at cpu_bytes_per_s (packed bytes per second): the
+ * share at which both channels finish together, f = B_P / (B_P + B_C), i.e.
+ * f / (1 - f) = B_P / B_C.  0 if both rates are 0 or one is negative. */
+double moe_copy_share(double pcie_bytes_per_s, double cpu_bytes_per_s);
+
+/* One expert's FFN on the host CPU for the rows that chose it, accumulated
+ * into a host y:  y[row_ids[j]] += row_w[j] * W_down (silu(W_gate x) * (W_up x))
+ * with x = x_bf16[row_ids[j]].  gate / up / down are the expert's packed
+ * matrices in host memory (format fmt, [inter x hidden] / [hidden x inter]);
+ * decoding is exact and every sum is fp64, rounded to fp32 once when added.
+ * n_threads host threads (0: all).  MOE_ECODE if a code is invalid,
+ * MOE_EFORMAT / MOE_ESHAPE / MOE_EINVAL as moe_unpack. */
+int moe_cpu_expert_ffn(const moe_dims* dims, int32_t fmt, const void* gate, const void* up, const void* down,
+                       const void* x_bf16, int32_t n_rows, const int32_t* row_ids, const float* row_w, float* y,
+                       int32_t n_threads);
+
+/* The end of a layer step computed in parts, on the device, asynchronous on
+ * `stream`:  y += add (add NULL: nothing added), then, when x_next is not
+ * NULL, x_next = bf16 (round to nearest even) of y + noise (noise NULL: 0),
+ * as moe_stack_decode chains layers.  All arrays [n] on the device. */
+int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, size_t n, void* stream);
 
 #ifdef __cplusplus
 }

@@ -217,6 +217,58 @@ void allocator() {
                              nullptr, nullptr) == MOE_EINVAL, "no layers");
 }
 
+void offload() {
+  // the slot cache over a random sequence: every selected expert ends on the
+  // device or on the CPU, never both; bad input is rejected
+  moe_slot_cache* c = nullptr;
+  check(moe_cache_create(2, 32, 5, &c) == MOE_OK && c, "cache create");
+  std::mt19937 rng(5);
+  std::vector<int32_t> idx(16), slot_of(32), ce(16), cs(16), cpu(16), idx_gpu(16);
+  for (int step = 0; step < 200; ++step) {
+    const int rows = 1 + static_cast<int>(rng() % 4), k = 4;
+    for (int i = 0; i < rows * k; ++i) idx[i] = static_cast<int32_t>(rng() % 32);
+    int32_t nc = 0, nu = 0;
+    const double share = (rng() % 5) / 4.0;
+    check(moe_cache_plan(c, step % 2, rows, k, idx.data(), share, slot_of.data(), ce.data(), cs.data(), &nc,
+                         cpu.data(), &nu, idx_gpu.data()) == MOE_OK, "plan");
+    for (int i = 0; i < rows * k; ++i) {
+      bool on_cpu = false;
+      for (int j = 0; j < nu; ++j) on_cpu = on_cpu || cpu[j] == idx[i];
+      check(on_cpu != (slot_of[idx[i]] >= 0), "device xor cpu");
+      check(idx_gpu[i] == (on_cpu ? -1 : idx[i]), "idx_gpu");
+    }
+  }
+  idx[0] = 32;
+  int32_t nc = 0, nu = 0;
+  check(moe_cache_plan(c, 0, 1, 1, idx.data(), 1.0, slot_of.data(), ce.data(), cs.data(), &nc, cpu.data(), &nu,
+                       idx_gpu.data()) == MOE_EINVAL, "id out of range");
+  check(moe_cache_plan(c, 2, 1, 1, idx.data(), 1.0, slot_of.data(), ce.data(), cs.data(), &nc, cpu.data(), &nu,
+                       idx_gpu.data()) == MOE_EINVAL, "layer out of range");
+  moe_cache_destroy(c);
+  moe_slot_cache* none = nullptr;
+  check(moe_cache_create(1, 8, 0, &none) == MOE_EINVAL && !none, "no slots");
+  check(moe_copy_share(3.0, 1.0) == 0.75, "copy share");
+  // the host FFN on a small Q2_0 expert, one row
+  const moe_dims d{64, 64, 8, 2, 0};
+  const size_t nb = moe_packed_bytes(MOE_FMT_Q2_0, 64, 64);
+  std::vector<float> w(64 * 64);
+  std::normal_distribution<float> nd(0.0f, 0.02f);
+  for (float& v : w) v = nd(rng);
+  std::vector<uint8_t> m(nb);
+  check(moe_pack(MOE_FMT_Q2_0, w.data(), 64, 64, m.data(), nb, 1) == MOE_OK, "pack for ffn");
+  std::vector<uint16_t> x(2 * 64, 0x3f80);   // bf16 1.0
+  std::vector<float> y(2 * 64, 0.0f);
+  const int32_t row = 1;
+  const float rw = 0.5f;
+  check(moe_cpu_expert_ffn(&d, MOE_FMT_Q2_0, m.data(), m.data(), m.data(), x.data(), 1, &row, &rw, y.data(), 2) ==
+            MOE_OK, "cpu ffn");
+  bool row0_zero = true;
+  for (int i = 0; i < 64; ++i) row0_zero = row0_zero && y[i] == 0.0f;
+  check(row0_zero, "cpu ffn leaves other rows");
+  check(moe_cpu_expert_ffn(&d, 9, m.data(), m.data(), m.data(), x.data(), 1, &row, &rw, y.data(), 1) == MOE_EFORMAT,
+        "cpu ffn format");
+}
+
 void dims_checks() {
   const moe_dims good{5120, 2304, 384, 6, 0};
   check(moe::check_dims(&good, 8) == MOE_OK, "8 rows");
@@ -244,6 +296,7 @@ int main() {
   workspaces();
   dims_checks();
   allocator();
+  offload();
   if (failures) {
     std::fprintf(stderr, "%d check(s) failed\n", failures);
     return 1;

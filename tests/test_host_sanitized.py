@@ -1,7 +1,7 @@
 """The host code of libmoe (packer and argument / workspace validation) under
 AddressSanitizer and UndefinedBehaviorSanitizer: tests/host_check.cpp built
-with g++ together with pack.cpp, host_api.cpp and alloc.cpp (no HIP code is
-involved) and run on the CPU."""
+with g++ together with pack.cpp, host_api.cpp, alloc.cpp and offload.cpp (no
+HIP code is involved) and run on the CPU."""
 
 import os
 import shutil
@@ -23,7 +23,7 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
            "-I", os.path.join(ROOT, "include"),
            os.path.join(ROOT, "tests", "host_check.cpp"),
            os.path.join(CSRC, "pack.cpp"), os.path.join(CSRC, "host_api.cpp"),
-           os.path.join(CSRC, "alloc.cpp"),
+           os.path.join(CSRC, "alloc.cpp"), os.path.join(CSRC, "offload.cpp"),
            "-pthread", "-o", str(exe)]
     build = subprocess.run(cmd, capture_output=True, text=True)
     assert build.returncode == 0, build.stdout + build.stderr

@@ -23,7 +23,7 @@ def L():
 
 def test_exports_match_header(L):
     hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
-    declared = set(re.findall(r"^\s*(?:const char\*|size_t|int32_t|int)\s+(moe_\w+)\s*\(", hdr, re.M))
+    declared = set(re.findall(r"^\s*(?:const char\*|size_t|int32_t|int|void|double)\s+(moe_\w+)\s*\(", hdr, re.M))
     assert declared == set(L.EXPORTS)
     for name in declared:
         assert hasattr(L.lib(), name), name
