@@ -60,7 +60,13 @@ def parse():
     p.add_argument("--workload", default="mixed_verify",
                    choices=["mixed_verify", "decode_q2", "fp4_layer", "draft128", "stack40_mixed",
                             "fp4_stack20", "fp4_prefill", "verify_correlated", "policy_stack40",
-                            "alloc_stack40"])
+                            "alloc_stack40", "offload_fp4"])
+    p.add_argument("--offload-layers", type=int, default=4,
+                   help="offload_fp4: FP4 layers whose routed experts live in pinned host memory")
+    p.add_argument("--offload-slots", type=int, default=384,
+                   help="offload_fp4: device expert slots (default: one layer's worth)")
+    p.add_argument("--offload-share", type=float, default=-1.0,
+                   help="offload_fp4: share of misses copied; negative: measured (moe_copy_share)")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="run one device copy of this many MiB first (a known-size reference "
                         "for hardware byte counters)")
@@ -714,6 +720,97 @@ def bench_alloc(args, torch, L, LY, synth):
     print(json.dumps(line), flush=True)
 
 
+def bench_offload(args, torch, L, LY, synth):
+    """FP4 layers of the real shape whose routed experts live in pinned host
+    memory, decoded through a device slot cache that holds a fraction of them
+    (default: 384 slots for 4 x 384 experts): per layer step the route, the
+    plan, the copies over PCIe and / or the host FFN, the device FFN and the
+    add.  Wall-clock time per chained pass (the step synchronises on the
+    selection)."""
+    from bit_moe_expert_02_amd import offload as OFL
+    base = synth.WORKLOADS["fp4_stack20"]
+    H, I, E, k = base.hidden, base.inter, base.n_experts, base.top_k
+    n_layers = args.offload_layers
+    fmt = "MXFP4"
+    lay = OFL.blob_layout(fmt, H, I)
+    t0 = time.perf_counter()
+    blobs = []
+    for i in range(8):   # distinct packed experts; slot e of layer l holds item (l * E + e) % 8
+        b = np.zeros(lay[3], np.uint8)
+        for o, m in zip(lay[:3], synth.expert_weights(base, LY.pool_layer(0, fmt), i)):
+            pk = L.pack(fmt, m)
+            b[o:o + pk.size] = pk
+        blobs.append(b)
+
+    def fill(li, e, dst):
+        dst[:] = blobs[(li * E + e) % len(blobs)]
+
+    routers = [torch.from_numpy(synth.router(base, li)).cuda() for li in range(n_layers)]
+    share = None if args.offload_share < 0 else args.offload_share
+    st = OFL.OffloadStack(H, I, E, k, routers, [None] * n_layers, [None] * n_layers,
+                          [[fmt] * E for _ in range(n_layers)], fill, args.offload_slots,
+                          copy_share=share, cpu_threads=0)
+    say(f"offload: {n_layers} layers, {st.store.numel() / 1e9:.1f} GB pinned, {st.n_slots} slots "
+        f"({st.n_slots * st.slot_bytes / 1e9:.1f} GB), share {st.copy_share:.3f}, rates {st.rates}, "
+        f"set-up {time.perf_counter() - t0:.1f} s")
+    passes, warm = min(args.steps, 16), min(args.warmup, 2)
+    out_rows = {}
+    for rows in (1, 8):
+        noise = torch.from_numpy(np.stack([synth.noise(base, li, rows) for li in range(n_layers)])).cuda()
+        ws = LY.workspace(st.dims, rows)
+        times = []
+        for i in range(warm + passes):
+            x0 = torch.from_numpy(synth.x_bf16(base, 0, rows, 70_000 + i).view(np.int16).copy()).cuda()
+            if i == warm:
+                before = dict(st.stats)
+            torch.cuda.synchronize()
+            ta = time.perf_counter()
+            st.decode(x0, rows, noise, ws)
+            torch.cuda.synchronize()
+            if i >= warm:
+                times.append(time.perf_counter() - ta)
+        d = {key: st.stats[key] - before[key] for key in st.stats}
+        ms = float(np.mean(times)) * 1e3
+        steps = max(d["steps"], 1)
+        touched = d["hits"] + d["copies"] + d["cpu"]
+        out_rows[rows] = dict(
+            ms_per_pass=round(ms, 3), tokens_per_s=round(rows / (ms * 1e-3), 2),
+            p10_ms=round(float(np.percentile(times, 10)) * 1e3, 3),
+            p90_ms=round(float(np.percentile(times, 90)) * 1e3, 3),
+            experts_per_layer_step=round(touched / steps, 2),
+            hit_rate=round(d["hits"] / max(touched, 1), 4),
+            copies_per_layer_step=round(d["copies"] / steps, 2),
+            cpu_per_layer_step=round(d["cpu"] / steps, 2),
+            copy_GBps_over_pass=round(d["copy_bytes"] / (sum(times)) / 1e9, 2),
+            cpu_seconds_per_pass=round(d["cpu_seconds"] / passes, 4))
+        say(f"offload rows {rows}: {ms:.2f} ms/pass, {out_rows[rows]}")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(base, 1, n_layers)
+    r0 = out_rows[1]
+    line = {
+        "metric": f"offloaded FP4 stack chained decode tokens/s ({n_layers} layers, experts in pinned host memory)",
+        "value": r0["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": passes, "warmup": warm,
+        "ms_per_step": r0["ms_per_pass"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4 codes x f16 -> f32 (router f64); host FFN f64",
+        "data": "synthetic (seeded; expert slots filled from 8 distinct packed experts)",
+        "config": {"workload": "offload_fp4", "layers": n_layers, "experts": n_layers * E,
+                   "store_GB": round(st.store.numel() / 1e9, 2), "slots": st.n_slots,
+                   "slot_GB": round(st.n_slots * st.slot_bytes / 1e9, 2),
+                   "copy_share": round(st.copy_share, 4),
+                   "measured_rates_GBps": None if st.rates is None else
+                   {key: round(v / 1e9, 3) for key, v in st.rates.items()},
+                   "rows": out_rows},
+        "roofline": {"bound": "pcie", "achieved": r0["copy_GBps_over_pass"],
+                     "peak": None if st.rates is None else round(st.rates["pcie_bytes_per_s"] / 1e9, 2),
+                     "unit": "GB/s", "frac": None if st.rates is None else
+                     round(r0["copy_GBps_over_pass"] * 1e9 / st.rates["pcie_bytes_per_s"], 4),
+                     "traffic": None, "kernel": "pinned host -> device copies over the pass "
+                                                "(peak: the measured pinned copy rate)"},
+        "cpu_baseline": cpu,
+    }
+    st.close()
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -745,6 +842,8 @@ def main():
         return bench_policy(args, torch, L, LY, synth)
     if args.workload == "alloc_stack40":
         return bench_alloc(args, torch, L, LY, synth)
+    if args.workload == "offload_fp4":
+        return bench_offload(args, torch, L, LY, synth)
     return main_decode(args, torch, L, LY, synth)
 
 

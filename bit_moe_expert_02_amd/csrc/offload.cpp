@@ -91,11 +91,20 @@ extern "C" int moe_cache_plan(moe_slot_cache* c, int32_t layer, int32_t rows, in
     if (s >= 0) c->last_use[s] = c->clock;   // hit
     else misses.push_back({e, cnt[static_cast<size_t>(e)]});
   }
-  // q = the rounded share of the misses that are copied: those used by the
-  // most pairs (then the lower id), since each saves the CPU the most work
+  // q of the m misses are copied: with f = copy_share the copies take time
+  // proportional to q (1 - f) and the CPU's experts (m - q) f, so q is the
+  // whole number next to m f (below or above) with the smaller larger time,
+  // the larger q on a tie.  The copied misses are those used by the most
+  // pairs (then the lower id), since each saves the CPU the most work.
   const int32_t m = static_cast<int32_t>(misses.size());
-  int32_t q = static_cast<int32_t>(std::floor(static_cast<double>(m) * copy_share + 0.5));
-  q = std::min(std::max(q, 0), m);
+  const double f = copy_share;
+  const double mf = static_cast<double>(m) * f;
+  const int32_t lo = std::min(m, std::max(0, static_cast<int32_t>(std::floor(mf))));
+  const int32_t hi = std::min(m, lo + 1);
+  auto cost = [&](int32_t qq) {
+    return std::max(static_cast<double>(qq) * (1.0 - f), static_cast<double>(m - qq) * f);
+  };
+  const int32_t q = cost(hi) <= cost(lo) ? hi : lo;
   std::stable_sort(misses.begin(), misses.end(),
                    [](const Miss& a, const Miss& b) { return a.rows > b.rows; });
   std::vector<uint8_t> on_cpu(static_cast<size_t>(c->E), 0);

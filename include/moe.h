@@ -412,9 +412,12 @@ void moe_cache_destroy(moe_slot_cache* cache);
 /* One layer step: which of the experts that idx selects are in a slot (hits),
  * which are copied into a slot now, and which the CPU computes.
  *   idx         host [rows x top_k], every id in [0, n_experts)
- *   copy_share  0 .. 1: the share of the step's misses to copy (rounded to
- *               the nearest count, halves up); moe_copy_share gives it from
- *               measured bandwidths
+ *   copy_share  0 .. 1: the share f of the step's m misses to copy;
+ *               moe_copy_share gives it from measured bandwidths.  The count
+ *               copied is the whole number q next to m f (below or above)
+ *               for which max(q (1 - f), (m - q) f) -- the slower of the two
+ *               channels, in units of an expert's time -- is smaller, the
+ *               larger q on a tie
  * Misses are copied in order of most pairs, then lower id.  A copy takes a
  * free slot (lowest index), else the least recently used slot (lowest index
  * on ties) that this step's experts do not use; when none is left the miss

@@ -15,7 +15,9 @@ Readings where the pages are silent (each also in the design notes):
   * f = B_P / (B_P + B_C): the share at which copies and CPU work end
     together (it solves f / (1 - f) = B_P / B_C; for B_P << B_C it is the
     page's m * B_P / B_H);
-  * q = m * f rounded to the nearest integer, halves up;
+  * q is a whole number of experts: of the two next to m * f, the one whose
+    slower channel finishes first (copies take time in proportion to
+    q * (1 - f), the CPU's experts (m - q) * f), the larger on a tie;
   * the copied misses are those chosen by the most pairs of the step, then
     the lower expert id; the rest go to the CPU;
   * a copy takes a free slot (lowest index), else the least recently used
@@ -27,7 +29,6 @@ cpu_expert_ffn: the CPU tier's arithmetic is the expert FFN of oracle.moe
 (parity of the library's CPU FFN is checked against moe.expert_ffn).
 """
 
-import math
 
 
 class SlotCache:
@@ -75,7 +76,15 @@ class SlotCache:
             else:
                 misses.append(e)
         m = len(misses)
-        q = min(max(int(math.floor(m * copy_share + 0.5)), 0), m)
+        f = copy_share
+        best = None
+        for cand in range(m + 1):                      # brute force over every count
+            if abs(cand - m * f) >= 1.0:
+                continue                               # only the two next to m * f
+            t = max(cand * (1 - f), (m - cand) * f)
+            if best is None or t < best[0] or (t == best[0] and cand > best[1]):
+                best = (t, cand)
+        q = best[1]
         misses.sort(key=lambda e: (-count[e], e))
         copies, cpu = [], []
         for j, e in enumerate(misses):

@@ -32,8 +32,10 @@ def test_oracle_hand_worked_sequence():
     # so the lower index (slot 1, expert 1) is evicted
     slot_of, copies, cpu, idx_gpu = c.plan(0, [[2, 7]], 1.0)
     assert copies == [(7, 1)] and cpu == [] and slot_of[1] == -1 and slot_of[7] == 1
-    # step 3, share 0.5: 5 hits slot 2; misses 1, 3, 4 (one pair each) ->
-    # q = floor(3 * 0.5 + 0.5) = 2: 1 and 3 are copied, 4 goes to the CPU.
+    # step 3, share 0.5: 5 hits slot 2; misses 1, 3, 4 (one pair each); m f =
+    # 1.5, and q = 1 or q = 2 both leave the slower channel at one expert's
+    # time (max(0.5, 1) = max(1, 0.5)), so the larger: 1 and 3 are copied,
+    # 4 goes to the CPU.
     # For 1: slots 0 and 1 were last used at step 2 -> slot 0 (expert 2 out);
     # for 3: slot 1 (expert 7 out), slots 0 and 2 are in use by this step
     slot_of, copies, cpu, idx_gpu = c.plan(0, [[1, 5], [3, 4]], 0.5)
@@ -77,7 +79,7 @@ def test_oracle_invariants_random():
                                                       resident.get((layer, e)) is None)
         assert [[(-1 if e in cpu else e) for e in row] for row in idx] == idx_gpu
         misses = len(copies) + len(cpu)
-        assert len(copies) <= int(np.floor(misses * share + 0.5))
+        assert len(copies) <= int(np.ceil(misses * share))
         for e, s in copies:
             resident = {k2: v for k2, v in resident.items() if v != s}
             resident[(layer, e)] = s
@@ -85,6 +87,29 @@ def test_oracle_invariants_random():
         assert len(set(resident.values())) == len(resident) <= S and len(owned) == len(resident)
         for e in range(E):
             assert slot_of[e] == resident.get((layer, e), -1)
+
+
+def _count_copied(m, f):
+    c = OO.SlotCache(1, m, m)
+    _, copies, cpu, _ = c.plan(0, [list(range(m))], f)
+    return len(copies)
+
+
+def test_oracle_copied_count_balances_the_channels():
+    """The number copied, worked by hand: q next to m f minimising
+    max(q (1 - f), (m - q) f)."""
+    # m f = 44.28: q = 44 leaves one expert on the CPU (time 0.984 of an
+    # expert), q = 45 leaves the copies at 45 * 0.016 = 0.72: copy all
+    assert _count_copied(45, 0.984) == 45
+    # the share one engine's profile chose ([P1 §3C], 14.7 %): m = 10 ->
+    # q = 1 (max(0.853, 1.323)) beats q = 2 (max(1.706, 1.176))
+    assert _count_copied(10, 0.147) == 1
+    assert _count_copied(4, 0.5) == 2 and _count_copied(7, 0.0) == 0 and _count_copied(7, 1.0) == 7
+    for m in range(0, 30):
+        for f in (0.05, 0.3, 0.5, 0.77, 0.95):
+            q = _count_copied(m, f)
+            best = min(max(c * (1 - f), (m - c) * f) for c in range(m + 1))
+            assert max(q * (1 - f), (m - q) * f) == pytest.approx(best, abs=1e-12)
 
 
 def test_copy_share_balance():
