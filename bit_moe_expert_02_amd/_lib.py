@@ -118,7 +118,7 @@ def lib():
         L.moe_cpu_expert_ffn.restype = ctypes.c_int
         L.moe_cpu_expert_ffn.argtypes = [dims_p, i32, vp, vp, vp, vp, i32, vp, vp, vp, i32]
         L.moe_add_chain.restype = ctypes.c_int
-        L.moe_add_chain.argtypes = [vp, vp, vp, vp, sz, vp]
+        L.moe_add_chain.argtypes = [vp, vp, vp, vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -350,5 +350,8 @@ def cpu_expert_ffn(d, fmt, gate, up, down, x_bf16, row_ids, row_w, y, nthreads=0
 
 
 def moe_add_chain(y, add, noise, x_next, stream=None):
+    """y [rows, hidden] fp32 device tensor; add / noise likewise or None; x_next
+    [rows, hidden] int16 (bf16 bits) or None."""
+    rows, hidden = y.shape
     _check("moe_add_chain", lib().moe_add_chain(_ptr(y), _ptr(add), _ptr(noise), _ptr(x_next),
-                                                y.numel(), _stream(stream)))
+                                                int(rows), int(hidden), _stream(stream)))

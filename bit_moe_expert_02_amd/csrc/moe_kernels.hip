@@ -101,8 +101,6 @@ struct Args {
   int base_b, nb;                 // fused launch: first worker workgroup, number of workers
   int nsw;                        // fused launch: workers that take the shared gate/up tiles
   // stack decode: the fused combine also writes the next layer's input
-  const float* noise;             // [R x H] fp32 added to y before rounding, or null
-  uint16_t* x_next;               // [R x H] bf16 out, or null
   int shared_early;               // 1: the shared expert's gate/up runs beside the router
                                   // (moe_layer), so the gate/up launch skips it
   int base_y;                     // fused launch: first combine workgroup
@@ -1295,9 +1293,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_down(Args a) {
 
 // Output element i = (r, n) of the fused launch: the row's k partials in
 // ascending expert id (ids from the published selection), then the shared
-// expert; every input is a tagged word of this call.  In a stack decode it
-// also writes the next layer's input.  A call in which a hand-off wait gave
-// up yields NaN (as far as this element can tell).
+// expert; every input is a tagged word of this call.  A call in which a
+// hand-off wait gave up yields NaN (as far as this element can tell).
 template <class S>
 __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) {
   if (i >= a.R * S::kH) return;
@@ -1332,12 +1329,6 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
   if (a.shared) s += __builtin_bit_cast(float, w[2 * kMaxK]);
   if (!got || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
   a.y[i] = s;
-  if (a.x_next) {   // stack decode: x_{l+1} = bf16 (round to nearest even) of the fp32 y + noise
-    const float v = a.noise ? s + a.noise[i] : s;
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
-    a.x_next[i] = static_cast<uint16_t>(u >> 16);
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1507,23 +1498,58 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   a.y[i] = bad ? __builtin_nanf("") : s;
 }
 
-// y += add (when given), then, when x_next is given, x_next = bf16 (round to
-// nearest even) of y + noise: the end of a layer step whose outputs were
-// computed in parts.
-__global__ __launch_bounds__(kThreads) void k_add_chain(float* y, const float* add, const float* noise,
-                                                        uint16_t* x_next, size_t n) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + tid();
-  if (i >= n) return;
-  float s = y[i];
-  if (add) {
-    s += add[i];
-    y[i] = s;
+// The end of a layer step, one workgroup per row of H: y += add (when
+// given); then, when x_next is given, the next layer's input: v = y + noise
+// (one fp32 addition), divided by 2^s when the row's largest |v| is 4 or more
+// (s = floor(log2 max|v|) - 1 brings it into [2, 4); s = 0 if the row holds a
+// NaN or an infinity), rounded to bf16 (nearest even).  A power of two keeps
+// the step exact and its decision free of summation order.
+__global__ __launch_bounds__(kThreads) void k_chain_rows(float* y, const float* add, const float* noise,
+                                                         uint16_t* x_next, int H) {
+  const size_t base = static_cast<size_t>(blockIdx.x) * H;
+  float* yr = y + base;
+  float m = 0.0f;
+  bool odd = false;   // a NaN or an infinity in the row
+  for (int i = tid(); i < H; i += kThreads) {
+    float v = yr[i];
+    if (add) {
+      v += add[base + i];
+      yr[i] = v;
+    }
+    if (x_next) {
+      if (noise) v += noise[base + i];
+      const float av = __builtin_fabsf(v);
+      odd = odd || !(av <= 3.4028234663852886e38f);
+      m = av > m ? av : m;
+    }
   }
-  if (x_next) {
-    const float v = noise ? s + noise[i] : s;
+  if (!x_next) return;
+  __shared__ float wm[kThreads / 64];
+  __shared__ int wodd[kThreads / 64];
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(m, o, 64);
+    m = t > m ? t : m;
+  }
+  const bool any_odd = __ballot(odd) != 0;
+  if ((tid() & 63) == 0) {
+    wm[tid() >> 6] = m;
+    wodd[tid() >> 6] = any_odd ? 1 : 0;
+  }
+  __syncthreads();
+  float mm = 0.0f;
+  int bad = 0;
+  for (int w = 0; w < kThreads / 64; ++w) {
+    mm = wm[w] > mm ? wm[w] : mm;
+    bad |= wodd[w];
+  }
+  const int sh = (!bad && mm >= 4.0f) ? ilogbf(mm) - 1 : 0;
+  for (int i = tid(); i < H; i += kThreads) {
+    float v = yr[i];
+    if (noise) v += noise[base + i];
+    v = __builtin_ldexpf(v, -sh);
     uint32_t u = __builtin_bit_cast(uint32_t, v);
     u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
-    x_next[i] = static_cast<uint16_t>(u >> 16);
+    x_next[base + i] = static_cast<uint16_t>(u >> 16);
   }
 }
 
@@ -1811,19 +1837,12 @@ int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn,
   return MOE_OK;
 }
 
-// Chained stack decode: where the fused combine writes the next layer's input.
-struct Chain {
-  const float* noise;
-  uint16_t* x_next;
-};
-
 // fused_only: the workspace holds only the fused launch's area (the fixed
 // workspace of moe_layer_noalloc, lay::fused_layout), not a full decode layout.
 int run(const moe_dims* d, const void* x, int rows, const float* w_router, const float* bias,
         const void* weights, const moe_expert_ref* experts, const moe_expert_ref* shared,
         int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes, void* stream,
-        bool route, bool ffn, void* const* events, int n_events, const Chain* chain = nullptr,
-        bool fused_only = false) {
+        bool route, bool ffn, void* const* events, int n_events, bool fused_only = false) {
   int st = check_dims(d, rows);
   if (st) return st;
   if (rows == 0) return MOE_OK;
@@ -1867,10 +1886,6 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   a.k = d->top_k;
   a.E = d->n_experts;
   a.shared_early = (route && ffn && shared) ? 1 : 0;
-  if (chain) {
-    a.noise = chain->noise;
-    a.x_next = chain->x_next;
-  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (route && ffn) {
     switch (shape_class(d)) {
@@ -1998,13 +2013,12 @@ int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t grid,
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 
-int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, size_t n, void* stream) {
-  if (!y) return MOE_EINVAL;
-  if (n == 0) return MOE_OK;
-  const size_t blocks = (n + moe::dev::kThreads - 1) / moe::dev::kThreads;
-  if (blocks > 0x7fffffffu) return MOE_EINVAL;
-  hipLaunchKernelGGL(moe::dev::k_add_chain, dim3(static_cast<unsigned>(blocks)), dim3(moe::dev::kThreads), 0,
-                     static_cast<hipStream_t>(stream), y, add, noise, static_cast<uint16_t*>(x_next), n);
+int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, int32_t rows, int32_t hidden,
+                  void* stream) {
+  if (!y || rows < 0 || hidden <= 0) return MOE_EINVAL;
+  if (rows == 0 || (!add && !x_next)) return MOE_OK;
+  hipLaunchKernelGGL(moe::dev::k_chain_rows, dim3(static_cast<unsigned>(rows)), dim3(moe::dev::kThreads), 0,
+                     static_cast<hipStream_t>(stream), y, add, noise, static_cast<uint16_t*>(x_next), hidden);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 
@@ -2052,7 +2066,7 @@ int moe_layer_noalloc(const moe_dims* dims, const void* x_bf16, int32_t rows, co
   uint8_t* ws = moe::scratch_ptr();
   if (!ws) return MOE_EDEVICE;
   return moe::run(dims, x_bf16, rows, w_router, sel_bias, weights, experts, shared, idx, wts, y, ws,
-                  moe::kScratchBytes, stream, true, true, nullptr, 0, nullptr, true);
+                  moe::kScratchBytes, stream, true, true, nullptr, 0, true);
 }
 
 int moe_layer_profiled(const moe_dims* dims, const void* x_bf16, int32_t rows,
@@ -2079,11 +2093,13 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
   uint16_t* x = static_cast<uint16_t*>(x_all);
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer_weights& w = layers[l];
-    moe::Chain c{noise ? noise + l * xy : nullptr, x + (l + 1) * xy};
-    const int st = moe::run(dims, x + l * xy, rows, w.w_router, w.sel_bias, w.weights, w.experts,
-                            w.shared, idx_all ? idx_all + l * ik : nullptr,
-                            wts_all ? wts_all + l * ik : nullptr, y_all + l * xy, ws, ws_bytes,
-                            stream, true, true, nullptr, 0, &c);
+    int st = moe::run(dims, x + l * xy, rows, w.w_router, w.sel_bias, w.weights, w.experts, w.shared,
+                      idx_all ? idx_all + l * ik : nullptr, wts_all ? wts_all + l * ik : nullptr,
+                      y_all + l * xy, ws, ws_bytes, stream, true, true, nullptr, 0);
+    if (st) return st;
+    if (rows == 0) continue;
+    st = moe_add_chain(y_all + l * xy, nullptr, noise ? noise + l * xy : nullptr, x + (l + 1) * xy, rows,
+                       dims->hidden, stream);
     if (st) return st;
   }
   return MOE_OK;

@@ -329,7 +329,15 @@ typedef struct {
 /* Decode rows through a stack of layers, each layer's output (plus noise)
  * feeding the next, as in the stacked-layer decode workloads:
  *     y_l     = moe_layer(layer l, x_l)
- *     x_{l+1} = bf16(y_l + noise_l)   (fp32 sum, then round to nearest even)
+ *     v       = y_l + noise_l          (one fp32 addition per element)
+ *     x_{l+1} = bf16(v / 2^s)          (round to nearest even), per row:
+ *               s = floor(log2 max|v|) - 1 when the row's largest |v| is 4
+ *               or more (it then lies in [2, 4)), else 0; s = 0 for a row
+ *               holding a NaN or an infinity.
+ * The power of two bounds each layer's input as a trained stack's
+ * normalisation would (synthetic SwiGLU experts have a gain above one and a
+ * quadratic response: unbounded, x overflows bf16 within a few layers), and
+ * keeps the step exact and independent of summation order.
  *   layers   host array of n_layers layer descriptions (device pointers)
  *   x_all    [(n_layers + 1) x rows x H] bf16, device: the caller fills
  *            x_all[0]; the call writes x_all[1 .. n_layers]
@@ -337,8 +345,9 @@ typedef struct {
  *   y_all    [n_layers x rows x H] fp32, device, out: every layer's y
  *   idx_all, wts_all  [n_layers x rows x top_k], device, or NULL
  *   ws       as for moe_layer (one workspace serves every layer)
- * One launch per layer on `stream`, no host synchronisation.  Every layer
- * has the shape in dims.  Returns the first failing layer's status. */
+ * Two launches per layer on `stream` (the layer, then the chain step of
+ * moe_add_chain), no host synchronisation.  Every layer has the shape in
+ * dims.  Returns the first failing layer's status. */
 int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_weights* layers,
                      int32_t rows, void* x_all, const float* noise, float* y_all,
                      int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
@@ -452,10 +461,12 @@ int moe_cpu_expert_ffn(const moe_dims* dims, int32_t fmt, const void* gate, cons
                        int32_t n_threads);
 
 /* The end of a layer step computed in parts, on the device, asynchronous on
- * `stream`:  y += add (add NULL: nothing added), then, when x_next is not
- * NULL, x_next = bf16 (round to nearest even) of y + noise (noise NULL: 0),
- * as moe_stack_decode chains layers.  All arrays [n] on the device. */
-int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, size_t n, void* stream);
+ * `stream`, one workgroup per row:  y += add (add NULL: nothing added); then,
+ * when x_next is not NULL, x_next = the next layer's input from y + noise
+ * (noise NULL: 0) exactly as moe_stack_decode chains layers.  y, add, noise:
+ * [rows x hidden] fp32; x_next [rows x hidden] bf16; all on the device. */
+int moe_add_chain(float* y, const float* add, const float* noise, void* x_next, int32_t rows, int32_t hidden,
+                  void* stream);
 
 #ifdef __cplusplus
 }

@@ -287,10 +287,31 @@ def round_bf16(v):
 
 
 def chain_next(y, eps):
-    """The next layer's input in a stacked decode: bf16 of the fp32 sum y + eps.
+    """The next layer's input in a stacked decode (the workload feeds each
+    layer's output plus Gaussian noise to the next layer).
 
-    y and eps are fp32; the sum is one IEEE fp32 addition, then rounded to
-    bf16 (the workload feeds each layer's output plus Gaussian noise to the
-    next layer).  Returns fp64 values."""
+    v = y + eps, one IEEE fp32 addition per element (y, eps fp32, [R, H] or
+    one row [H]); per row, when the largest |v| is 4 or more, v is divided by
+    2^s with s = floor(log2 max|v|) - 1, which brings that largest value into
+    [2, 4) (s = 0 for a row holding a NaN or an infinity); then bf16, round to
+    nearest even.  Returns fp64 values.
+
+    Reading: a trained stack keeps every layer's input bounded (its layers
+    normalise their inputs).  Synthetic N(0, 0.02^2) SwiGLU experts have a
+    gain above one and a quadratic response: chained unbounded, x overflows
+    bf16 within a few layers and the routing degenerates.  Dividing by a power
+    of two chosen from the row's maximum is exact and does not depend on any
+    summation order."""
     s = np.asarray(y, np.float32) + np.asarray(eps, np.float32)
-    return round_bf16(s.astype(np.float64))
+    v = s.astype(np.float64)
+    rows = np.atleast_2d(v)
+    out = np.empty_like(rows)
+    for r in range(rows.shape[0]):
+        with np.errstate(invalid="ignore"):
+            m = np.max(np.abs(rows[r]))
+        sh = 0
+        if np.isfinite(m) and m >= 4.0:
+            _, ex = np.frexp(m)             # m = f * 2^ex, f in [0.5, 1): floor(log2 m) = ex - 1
+            sh = int(ex) - 2
+        out[r] = round_bf16(np.ldexp(rows[r], -sh))
+    return out.reshape(v.shape)

@@ -51,3 +51,28 @@ def test_chain_next_adds_in_fp32_then_rounds():
     e = np.array([2.0 ** -24, 2.0 ** -8, 1.0, 0.5], np.float32)
     # 1 + 2^-24 rounds to 1 in fp32 before bf16 sees it; 1 + 2^-8 is a bf16 tie -> 1
     np.testing.assert_array_equal(OM.chain_next(y, e), [1.0, 1.0, 1.0, -2.0])
+
+
+def test_chain_next_bounds_rows_by_a_power_of_two():
+    """Rows whose largest |y + eps| is below 4 pass unscaled; a row reaching 4
+    is halved; 100 goes to 100 / 32 = 3.125 (floor(log2 100) = 6, s = 5);
+    each row has its own power; a NaN or an infinity leaves its row unscaled."""
+    z = np.zeros(4, np.float32)
+    rows = np.array([[3.99, -1.0, 0.5, 0.25],
+                     [4.0, -1.0, 0.5, 0.25],
+                     [-100.0, 3.0, 0.5, 1.0],
+                     [np.nan, 8.0, 2.0, 1.0],
+                     [np.inf, 8.0, 2.0, 1.0]], np.float32)
+    out = OM.chain_next(rows, np.zeros_like(rows))
+    np.testing.assert_array_equal(out[0], OM.round_bf16(rows[0].astype(np.float64)))
+    np.testing.assert_array_equal(out[1], [2.0, -0.5, 0.25, 0.125])
+    np.testing.assert_array_equal(out[2], OM.round_bf16(np.array([-3.125, 3 / 32, 0.5 / 32, 1 / 32])))
+    assert np.isnan(out[3, 0]) and np.array_equal(out[3, 1:], [8.0, 2.0, 1.0])
+    assert np.isinf(out[4, 0]) and np.array_equal(out[4, 1:], [8.0, 2.0, 1.0])
+    # a power of two commutes with the rounding: the bound only moves the exponent
+    g = np.random.default_rng(2).standard_normal((3, 64)).astype(np.float32) * np.float32(50)
+    o = OM.chain_next(g, z[:1].repeat(64)[None, :].repeat(3, 0))
+    for r in range(3):
+        sh = int(np.floor(np.log2(np.abs(g[r]).max()))) - 1
+        np.testing.assert_array_equal(o[r], OM.round_bf16(g[r].astype(np.float64)) / 2.0 ** sh)
+        assert 2.0 <= np.abs(o[r]).max() < 4.0
