@@ -102,7 +102,7 @@ struct GenEntry {
 // leave a word there that a later fused call would take for its own.
 // ---------------------------------------------------------------------------
 struct TaggedLayout {
-  size_t err, lgt, selt, ht, part_t, end;
+  size_t err, lgt, selt, ht, part_t, rmax, end;
 };
 
 struct DecodeLayout {       // moe_route / moe_expert_ffn / moe_layer, rows <= kMaxRows
@@ -133,6 +133,8 @@ constexpr TaggedLayout tagged_layout(const moe_dims& d) {
   l.selt = o;     o = align256(o + 8 * static_cast<size_t>(kSelRep) * kSelRepWords);
   l.ht = o;       o = align256(o + 8 * pairs * d.inter);
   l.part_t = o;   o = align256(o + 8 * pairs * d.hidden);
+  // stack decode: each combine workgroup's largest |y + noise| in its row
+  l.rmax = o;     o = align256(o + 8 * static_cast<size_t>(kMaxRows) * ((d.hidden + kThreads - 1) / kThreads));
   l.end = o;
   return l;
 }

@@ -95,6 +95,9 @@ struct Args {
   uint32_t* err;                  // [1] the tag of a call in which a wait gave up
   int spin_limit;                 // polls before a hand-off wait gives up
   uint64_t* part_t;               // [(R*k + R) x H] partial outputs as tagged fp32
+  uint64_t* rmax_t;               // [R x H / kThreads] per combine workgroup: max |y + noise| (stack decode)
+  const float* noise;             // stack decode: [R x H] fp32 added to y, or null
+  uint16_t* x_next;               // stack decode: [R x H] the next layer's bf16 input, or null
   uint64_t* lgt;                  // [R x E x 2] logits as tagged halves (low, high)
   uint64_t* selt;                 // kSelRep copies of [R x k x kSelWords] selection entries
   uint64_t* ht;                   // [(R*k + R) x I] h as tagged fp32
@@ -1291,13 +1294,32 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_down(Args a) {
   run_items<S, 0, false>(a, a.slots, blockIdx.x, gridDim.x, lds);
 }
 
+// The bf16 (round to nearest even) bits of v.
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// The power of two 2^s that bounds a row of the next layer's input (s = 0 if
+// the row's largest |v| is below 4 or the row holds a NaN or an infinity).
+__device__ __forceinline__ int chain_shift(float m, bool odd) {
+  return (!odd && m >= 4.0f) ? ilogbf(m) - 1 : 0;
+}
+
 // Output element i = (r, n) of the fused launch: the row's k partials in
 // ascending expert id (ids from the published selection), then the shared
 // expert; every input is a tagged word of this call.  A call in which a
 // hand-off wait gave up yields NaN (as far as this element can tell).
+// Called by every thread of a combine workgroup (kThreads consecutive
+// elements of one row, since H is a multiple of kThreads).  In a stack decode
+// it also writes the next layer's input, x = bf16(v / 2^s), v = y + noise,
+// with s from the row's largest |v|: each workgroup publishes its share of
+// that maximum as a tagged word and reads its row's others.
 template <class S>
 __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) {
-  if (i >= a.R * S::kH) return;
+  static_assert(S::kH % kThreads == 0, "a combine workgroup lies in one row");
+  if (i >= a.R * S::kH) return;   // whole workgroups: the grid covers R * H exactly
   const int r = i / S::kH, n = i - r * S::kH;
   const int k = a.k;
   uint32_t w[2 * kMaxK + 1];
@@ -1329,6 +1351,55 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
   if (a.shared) s += __builtin_bit_cast(float, w[2 * kMaxK]);
   if (!got || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
   a.y[i] = s;
+  if (!a.x_next) return;
+  constexpr int NC = S::kH / kThreads;   // combine workgroups per row
+  const float v = a.noise ? s + a.noise[i] : s;
+  const float av = __builtin_fabsf(v);
+  bool odd = !(av <= 3.4028234663852886e38f);
+  float m = odd ? 0.0f : av;
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(m, o, 64);
+    m = t > m ? t : m;
+  }
+  odd = __ballot(odd) != 0;
+  __shared__ float wm[kThreads / 64];
+  __shared__ int wodd[kThreads / 64];
+  __shared__ int shift;
+  if ((tid() & 63) == 0) {
+    wm[tid() >> 6] = m;
+    wodd[tid() >> 6] = odd ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid() < 64) {
+    float mm = 0.0f;
+    int bad = 0;
+    for (int q = 0; q < kThreads / 64; ++q) {
+      mm = wm[q] > mm ? wm[q] : mm;
+      bad |= wodd[q];
+    }
+    // this workgroup's share: the maximum's bits, or a NaN pattern for a row
+    // holding a NaN or an infinity
+    uint64_t* row = a.rmax_t + static_cast<size_t>(r) * NC;
+    if (tid() == 0) tstore(row + n / kThreads, tag, bad ? 0x7FC00000u : __builtin_bit_cast(uint32_t, mm));
+    uint32_t pv[1];
+    const int lane = tid();
+    const bool got_all = __ballot(!await_batch<1>([row, lane](int) -> const uint64_t* {
+                                                    return lane < NC ? row + lane : nullptr;
+                                                  },
+                                                  tag, a.err, pv, a.spin_limit)) == 0;
+    const float pm = __builtin_bit_cast(float, pv[0]);
+    const bool podd = lane < NC && !(pm <= 3.4028234663852886e38f);
+    float rm = lane < NC && !podd ? pm : 0.0f;
+    for (int o = 32; o > 0; o >>= 1) {
+      const float t = __shfl_xor(rm, o, 64);
+      rm = t > rm ? t : rm;
+    }
+    // a wait that gave up leaves the row's bound unknown: its x is NaN
+    if (tid() == 0) shift = got_all ? chain_shift(rm, __ballot(podd) != 0) : 0x7fffffff;
+  }
+  __syncthreads();
+  const int sh = shift;
+  a.x_next[i] = sh == 0x7fffffff ? static_cast<uint16_t>(0x7FC0u) : bf16_rne(__builtin_ldexpf(v, -sh));
 }
 
 // ---------------------------------------------------------------------------
@@ -1542,14 +1613,11 @@ __global__ __launch_bounds__(kThreads) void k_chain_rows(float* y, const float* 
     mm = wm[w] > mm ? wm[w] : mm;
     bad |= wodd[w];
   }
-  const int sh = (!bad && mm >= 4.0f) ? ilogbf(mm) - 1 : 0;
+  const int sh = chain_shift(mm, bad != 0);
   for (int i = tid(); i < H; i += kThreads) {
     float v = yr[i];
     if (noise) v += noise[base + i];
-    v = __builtin_ldexpf(v, -sh);
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    u = (u & 0x7FFFFFFFu) > 0x7F800000u ? (u | 0x00400000u) : u + 0x7FFFu + ((u >> 16) & 1u);
-    x_next[base + i] = static_cast<uint16_t>(u >> 16);
+    x_next[base + i] = bf16_rne(__builtin_ldexpf(v, -sh));
   }
 }
 
@@ -1774,6 +1842,7 @@ int launch_fused(const moe_dims* d, int rows, dev::Args a, uint8_t* w8, const la
   a.lgt = reinterpret_cast<uint64_t*>(w8 + l.lgt);
   a.selt = reinterpret_cast<uint64_t*>(w8 + l.selt);
   a.ht = reinterpret_cast<uint64_t*>(w8 + l.ht);
+  a.rmax_t = reinterpret_cast<uint64_t*>(w8 + l.rmax);
   a.shared_early = 1;     // the shared gate/up tiles are taken by the workers before the selection
   a.base_b = d->n_experts + rows;
   a.nb = item_grid((sh ? S::MAX_TILES_GU : 0) + n_routed * S::MAX_TILES_GU + (n_routed + (sh ? 1 : 0)) * S::MAX_TILES_DN,
@@ -1842,7 +1911,8 @@ int launch_layer(const moe_dims* d, int rows, dev::Args a, bool route, bool ffn,
 int run(const moe_dims* d, const void* x, int rows, const float* w_router, const float* bias,
         const void* weights, const moe_expert_ref* experts, const moe_expert_ref* shared,
         int32_t* idx, float* wts, float* y, void* ws, size_t ws_bytes, void* stream,
-        bool route, bool ffn, void* const* events, int n_events, bool fused_only = false) {
+        bool route, bool ffn, void* const* events, int n_events, bool fused_only = false,
+        const float* noise = nullptr, uint16_t* x_next = nullptr) {
   int st = check_dims(d, rows);
   if (st) return st;
   if (rows == 0) return MOE_OK;
@@ -1886,6 +1956,8 @@ int run(const moe_dims* d, const void* x, int rows, const float* w_router, const
   a.k = d->top_k;
   a.E = d->n_experts;
   a.shared_early = (route && ffn && shared) ? 1 : 0;
+  a.noise = noise;
+  a.x_next = x_next;     // only the fused launch writes it
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (route && ffn) {
     switch (shape_class(d)) {
@@ -2093,13 +2165,10 @@ int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_wei
   uint16_t* x = static_cast<uint16_t*>(x_all);
   for (int l = 0; l < n_layers; ++l) {
     const moe_layer_weights& w = layers[l];
-    int st = moe::run(dims, x + l * xy, rows, w.w_router, w.sel_bias, w.weights, w.experts, w.shared,
-                      idx_all ? idx_all + l * ik : nullptr, wts_all ? wts_all + l * ik : nullptr,
-                      y_all + l * xy, ws, ws_bytes, stream, true, true, nullptr, 0);
-    if (st) return st;
-    if (rows == 0) continue;
-    st = moe_add_chain(y_all + l * xy, nullptr, noise ? noise + l * xy : nullptr, x + (l + 1) * xy, rows,
-                       dims->hidden, stream);
+    const int st = moe::run(dims, x + l * xy, rows, w.w_router, w.sel_bias, w.weights, w.experts, w.shared,
+                            idx_all ? idx_all + l * ik : nullptr, wts_all ? wts_all + l * ik : nullptr,
+                            y_all + l * xy, ws, ws_bytes, stream, true, true, nullptr, 0, false,
+                            noise ? noise + l * xy : nullptr, x + (l + 1) * xy);
     if (st) return st;
   }
   return MOE_OK;

@@ -345,9 +345,10 @@ typedef struct {
  *   y_all    [n_layers x rows x H] fp32, device, out: every layer's y
  *   idx_all, wts_all  [n_layers x rows x top_k], device, or NULL
  *   ws       as for moe_layer (one workspace serves every layer)
- * Two launches per layer on `stream` (the layer, then the chain step of
- * moe_add_chain), no host synchronisation.  Every layer has the shape in
- * dims.  Returns the first failing layer's status. */
+ * One launch per layer on `stream`, no host synchronisation: the layer's
+ * combine workgroups exchange their shares of each row's maximum through
+ * tagged words and write x_{l+1}.  Every layer has the shape in dims.
+ * Returns the first failing layer's status. */
 int moe_stack_decode(const moe_dims* dims, int32_t n_layers, const moe_layer_weights* layers,
                      int32_t rows, void* x_all, const float* noise, float* y_all,
                      int32_t* idx_all, float* wts_all, void* ws, size_t ws_bytes, void* stream);
