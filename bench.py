@@ -684,8 +684,11 @@ def bench_alloc(args, torch, L, LY, synth):
     t0 = time.perf_counter()
     names, cost, nbytes = L.allocate_formats(err, tokens, energy, nb)
     t_alloc = time.perf_counter() - t0
-    from oracle import alloc as OA
-    q2_cost = float(OA.costs(err, energy)[:, :, 1].sum())
+    # the same cost of the all-Q2_0 stack, for the ratio reported beside it:
+    # held-out error / layer energy, the first 2 and last 3 layers doubled
+    n_l = err.shape[0]
+    w_l = np.array([2.0 if (li < 2 or li >= n_l - 3) else 1.0 for li in range(n_l)])
+    q2_cost = float((w_l[:, None] * err[:, :, 1] / energy[:, None]).sum())
     budget = base.layers * base.n_experts * nb[1]
     shares = {f: round(float((names == f).mean()), 4) for f in ("TERN160", "Q2_0", "Q3")}
     say(f"allocation: cost {cost / q2_cost:.3f} of all-Q2_0, bytes {nbytes / budget:.5f} of budget, {shares}")
@@ -706,6 +709,7 @@ def bench_alloc(args, torch, L, LY, synth):
         say(f"allocated stack rows {rows}: {ms:.3f} ms/pass, {gbps:.0f} GB/s")
     cpu = None
     if not args.no_cpu_baseline:
+        from oracle import alloc as OA
         t1 = time.perf_counter()
         OA.allocate(err, tokens, energy, nb)
         t_oracle = time.perf_counter() - t1
