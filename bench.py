@@ -637,8 +637,9 @@ def bench_verify_correlated(args, torch, L, LY, synth):
                                  "r2": round(float(r2(a[:, 1], a[:, 2], d)), 4)},
            "pass_ms_at_6_7_rows": round(t67, 4),
            "tokens_per_s_at_3_39_accepted_per_pass": round(PAGES_TOKENS_PER_PASS / (t67 * 1e-3), 1)}
+    cpu = None if args.no_cpu_baseline else cpu_baseline(base, 1, base.layers)
     line = stack_line(args, base, out_rows, "verify-window decode: pass time vs rows on the 40-layer mixed stack "
-                      "(correlated rows)", extra_cfg=cfg)
+                      "(correlated rows)", extra_cfg=cfg, cpu=cpu)
     line["value"] = cfg["tokens_per_s_at_3_39_accepted_per_pass"]
     line["unit"] = "tokens/s (3.39 accepted tokens per pass at 6.7 rows)"
     print(json.dumps(line), flush=True)
@@ -667,9 +668,10 @@ def bench_policy(args, torch, L, LY, synth):
                                   frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
             say(f"policy x{scale} rows {rows}: {ms:.3f} ms/pass, {u:.1f} experts/layer")
         per_scale[str(scale)] = rows_out
+    cpu = None if args.no_cpu_baseline else cpu_baseline(base, 1, base.layers)
     line = stack_line(args, base, per_scale["0.5"], "policy_stack40 chained decode tokens/s (residency bias x0.5)",
                       extra_cfg={"by_scale": per_scale, "tiers_per_layer": list(synth.POLICY_TIERS),
-                                 "tier_bias": list(synth.POLICY_BIAS)})
+                                 "tier_bias": list(synth.POLICY_BIAS)}, cpu=cpu)
     print(json.dumps(line), flush=True)
 
 
@@ -707,15 +709,15 @@ def bench_alloc(args, torch, L, LY, synth):
                               pass_bytes=int(b), unique_experts_per_layer=round(u, 2), GBps=round(gbps, 1),
                               frac_of_hbm_peak=round(gbps / HBM_PEAK_GBPS, 4))
         say(f"allocated stack rows {rows}: {ms:.3f} ms/pass, {gbps:.0f} GB/s")
-    cpu = None
+    cpu, t_oracle = None, None
     if not args.no_cpu_baseline:
         from oracle import alloc as OA
         t1 = time.perf_counter()
         OA.allocate(err, tokens, energy, nb)
         t_oracle = time.perf_counter() - t1
-        cpu = dict(value=round(1.0 / t_oracle, 4), unit="allocations/s", cores=1, kind="oracle",
-                   sample=f"the oracle's allocation of the 40 x 384 stack, {t_oracle:.2f} s (library: {t_alloc:.3f} s)")
+        cpu = cpu_baseline(base, 1, base.layers)
     cfg = {"allocation": {"cost_vs_all_q2": round(cost / q2_cost, 4), "bytes": int(nbytes), "budget": int(budget),
+                          "oracle_seconds": None if t_oracle is None else round(t_oracle, 2),
                           "shares": shares, "max_ternary_share_per_layer":
                               round(float((names == "TERN160").mean(axis=1).max()), 4),
                           "library_seconds": round(t_alloc, 3)}}
