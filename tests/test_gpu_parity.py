@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
 from bit_moe_expert_02_amd import _lib as L          # noqa: E402
 from bit_moe_expert_02_amd import layer as LY        # noqa: E402
 from bit_moe_expert_02_amd import synth              # noqa: E402
+from oracle import moe as OM                         # noqa: E402
 
 
 def _say(*a):
@@ -164,6 +165,43 @@ def test_tiny_selection_limits():
     err = G.rel_l2_rows(gy, G.oracle_y(wl, 0, x, idx, w, list(range(8))))
     _say("  rel L2 per row", G.fmt_err(err))
     assert np.all(err <= G.REL_L2_TOL)
+
+
+def test_selection_exact_ties_and_lower_half_order():
+    """Keys that tie exactly, and keys equal in their upper 32 bits that
+    differ only below: a zero router (every logit 0) and a crafted bias, so
+    key = bias exactly.  Expected from the rules alone: equal keys go to the
+    lower id, so experts 5, 69, 133 (one lane of the selection wave, bias 2)
+    come first, then 10, 11, 300 (bias 1 + 3 * 2^-23, three lanes), then 21
+    (1 + 2 * 2^-23) and 20 (1 + 2^-23), whose keys differ only in their lower
+    32 bits; weights are all 1/8 (the unbiased logits are equal).  Through the
+    fused layer and the split route, 1 and 8 rows."""
+    wl = synth.Workload("tiny_ties", 13, 512, 256, 384, 8, "Q2_0", None, use_bias=True, rows=(8,))
+    bias = np.full(384, -1.0, np.float32)
+    bias[[5, 69, 133]] = 2.0
+    u = np.float32(2.0 ** -23)
+    bias[[10, 11, 300]] = np.float32(1.0) + 3 * u
+    bias[21] = np.float32(1.0) + 2 * u
+    bias[20] = np.float32(1.0) + u
+    want = [5, 69, 133, 10, 11, 300, 21, 20]
+    dl = LY.DeviceLayer(wl, 0, materialize=want)
+    dl.router.zero_()
+    dl.bias.copy_(torch.from_numpy(bias))
+    for rows in (1, 8):
+        xbits = synth.x_bf16(wl, 0, rows, 0)
+        oi, ow, _ = OM.select_experts(np.zeros((rows, 384)), 8, bias)
+        assert all(list(r) == want for r in oi)                     # the oracle agrees with the rules
+        gi, gw, gy, _ = G.run_layer(dl, G.device_inputs(wl, 0, xbits), rows)
+        assert np.array_equal(gi, oi), gi
+        np.testing.assert_array_equal(gw, np.full((rows, 8), 0.125, np.float32))
+        ref = G.oracle_y(wl, 0, OM.bf16_to_f64(xbits), oi, ow, list(range(rows)))
+        assert np.all(G.rel_l2_rows(gy, ref) <= G.REL_L2_TOL)
+        ws = LY.workspace(dl.dims, rows)
+        idx = torch.zeros((rows, 8), dtype=torch.int32, device="cuda")
+        wts = torch.zeros((rows, 8), dtype=torch.float32, device="cuda")
+        L.moe_route(dl.dims, G.device_inputs(wl, 0, xbits), rows, dl.router, dl.bias, idx, wts, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), oi)
 
 
 # ------------------------------------------------------------------ real shapes
