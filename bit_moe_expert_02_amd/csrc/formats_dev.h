@@ -36,14 +36,15 @@ __device__ __forceinline__ void rec_store(uint8_t* rec, int dw, uint32_t v) {
   reinterpret_cast<uint32_t*>(rec)[dw] = v;
 }
 
-// f16(v * 2^(10-p)) for a pair; accumulates S += x~ * (2^(10-p) + off)
-__device__ __forceinline__ uint32_t make_pair(float lo, float hi, int p, float off, float& s) {
-  const float sc = __builtin_ldexpf(1.0f, 10 - p);
+// f16(g * v * 2^(10-p)) for a pair (g: the row's power-of-two sigma);
+// accumulates S += x~ * (2^(10-p) + off) = x' * (1 + off * 2^(p-10)) over the
+// pair with one dot2: the factor is exact in f16 for every format's (p, off),
+// so both products are exact and S sees the rounded x' values, as the dot does.
+__device__ __forceinline__ uint32_t make_pair(float lo, float hi, float g, int p, float off, float& s) {
+  const float sc = g * __builtin_ldexpf(1.0f, 10 - p);
   const uint32_t pr = pack_h2(lo * sc, hi * sc);
-  const float k = sc + off;
-  const float inv = __builtin_ldexpf(1.0f, p - 10);
-  s = fmaf(h2_lo(pr) * inv, k, s);
-  s = fmaf(h2_hi(pr) * inv, k, s);
+  const float k = 1.0f + off * __builtin_ldexpf(1.0f, p - 10);
+  s = dot2(pr, pack_h2(k, k), s);
   return pr;
 }
 
@@ -71,10 +72,10 @@ struct FmtQ2 {
     r.s = bload16(m, static_cast<uint32_t>(nrows * nbu * 16) + bi * 2u);
   }
   // sub-unit d = code dword d: values 16d .. 16d+15
-  __device__ static __forceinline__ void prep_sub(const float (&v)[16], int d, uint8_t* rec) {
+  __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int d, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rec_store(rec, d * 8 + i, make_pair(v[i], v[i + 8], kP[i], 2.0f, s));
+    for (int i = 0; i < 8; ++i) rec_store(rec, d * 8 + i, make_pair(v[i], v[i + 8], g, kP[i], 2.0f, s));
     reinterpret_cast<float*>(rec)[32 + d] = s;
   }
   template <int RT, int NT>
@@ -159,12 +160,12 @@ struct FmtQ8 {
     r.s = bload16(m, static_cast<uint32_t>(nrows * nbu * 32) + bi * 2u);
   }
   // sub-unit h = code dwords 4h .. 4h+3: values 16h .. 16h+15
-  __device__ static __forceinline__ void prep_sub(const float (&v)[16], int h, uint8_t* rec) {
+  __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int h, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      rec_store(rec, 8 * h + 2 * d, make_pair(v[4 * d], v[4 * d + 2], 2, 128.0f, s));
-      rec_store(rec, 8 * h + 2 * d + 1, make_pair(v[4 * d + 1], v[4 * d + 3], 2, 128.0f, s));
+      rec_store(rec, 8 * h + 2 * d, make_pair(v[4 * d], v[4 * d + 2], g, 2, 128.0f, s));
+      rec_store(rec, 8 * h + 2 * d + 1, make_pair(v[4 * d + 1], v[4 * d + 3], g, 2, 128.0f, s));
     }
     reinterpret_cast<float*>(rec)[16 + h] = s;
   }
@@ -243,9 +244,9 @@ struct FmtMXFP4 {
     r.c[0] = q.x; r.c[1] = q.y; r.c[2] = q.z; r.c[3] = q.w;
     r.s = bload8(m, static_cast<uint32_t>(nrows * nbu * 16) + bi);
   }
-  __device__ static __forceinline__ void prep_sub(const float (&v)[16], int h, uint8_t* rec) {
+  __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int h, uint8_t* rec) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rec_store(rec, 8 * h + k, pack_h2(v[2 * k], v[2 * k + 1]));
+    for (int k = 0; k < 8; ++k) rec_store(rec, 8 * h + k, pack_h2(v[2 * k] * g, v[2 * k + 1] * g));
   }
   template <int RT, int NT>
   __device__ static __forceinline__ void dot(const Raw (&raw)[RT], const uint8_t* xr, int rstride,
@@ -332,17 +333,17 @@ struct FmtTern {
            (static_cast<uint32_t>(d[4]) << 4) | (static_cast<uint32_t>(d[4]) << 20);
   }
   // sub-unit q = code dword q = byte pairs 2q, 2q+1: values 20q .. 20q+19
-  __device__ static __forceinline__ void prep_sub(const float (&vv)[20], int q, uint8_t* rec) {
+  __device__ static __forceinline__ void prep_sub(const float (&vv)[20], float g, int q, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) {
       const int m = 2 * q + mm;
       const float* v = vv + 10 * mm;
-      rec_store(rec, 5 * m + 0, make_pair(v[0], v[1], 8, 1.0f, s));
-      rec_store(rec, 5 * m + 1, make_pair(v[2], v[3], 6, 1.0f, s));
-      rec_store(rec, 5 * m + 2, make_pair(v[5], v[6], 8, 1.0f, s));
-      rec_store(rec, 5 * m + 3, make_pair(v[7], v[8], 6, 1.0f, s));
-      rec_store(rec, 5 * m + 4, make_pair(v[4], v[9], 4, 1.0f, s));
+      rec_store(rec, 5 * m + 0, make_pair(v[0], v[1], g, 8, 1.0f, s));
+      rec_store(rec, 5 * m + 1, make_pair(v[2], v[3], g, 6, 1.0f, s));
+      rec_store(rec, 5 * m + 2, make_pair(v[5], v[6], g, 8, 1.0f, s));
+      rec_store(rec, 5 * m + 3, make_pair(v[7], v[8], g, 6, 1.0f, s));
+      rec_store(rec, 5 * m + 4, make_pair(v[4], v[9], g, 4, 1.0f, s));
     }
     reinterpret_cast<float*>(rec)[40 + q] = s;
   }
@@ -443,10 +444,10 @@ struct FmtQ3 {
     r.u24 = static_cast<uint32_t>(pair >> (24u * ku - 32u * w0)) & 0xFFFFFFu;
   }
   // sub-unit j = sub-block j: values 16j .. 16j+15
-  __device__ static __forceinline__ void prep_sub(const float (&v)[16], int j, uint8_t* rec) {
+  __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int j, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], kP[i], 4.0f, s));
+    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], g, kP[i], 4.0f, s));
     reinterpret_cast<float*>(rec)[32 + j] = s;
   }
   template <int RT, int NT>

@@ -333,10 +333,7 @@ __device__ __forceinline__ void build_records(const void* const* rows, int nb, c
     const int u = rem / F::SUBS, sub = rem - u * F::SUBS;
     float v[F::SUBV];
     load_vals<F::SUBV, KR, BF16, LDS>(rows[t], u * F::UNIT + sub * F::SUBV, v);
-    const float sg = __builtin_ldexpf(1.0f, sig_exp[t]);
-#pragma unroll
-    for (int i = 0; i < F::SUBV; ++i) v[i] *= sg;
-    F::prep_sub(v, sub, rec + t * RSTRIDE + u * F::XREC);
+    F::prep_sub(v, __builtin_ldexpf(1.0f, sig_exp[t]), sub, rec + t * RSTRIDE + u * F::XREC);
   }
 }
 
