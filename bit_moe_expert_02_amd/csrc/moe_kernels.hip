@@ -337,6 +337,20 @@ __device__ __forceinline__ void build_records(const void* const* rows, int nb, c
   }
 }
 
+// Records of one row (src) into LDS with sigma 2^se; every thread calls it
+// with the same se.
+template <class F, int KR, bool BF16, bool LDS = false>
+__device__ __forceinline__ void build_row_records(const void* src, int se, uint8_t* rec) {
+  constexpr int PER_ROW = F::units(KR) * F::SUBS;
+  const float g = __builtin_ldexpf(1.0f, se);
+  for (int item = tid(); item < PER_ROW; item += kThreads) {
+    const int u = item / F::SUBS, sub = item - u * F::SUBS;
+    float v[F::SUBV];
+    load_vals<F::SUBV, KR, BF16, LDS>(src, u * F::UNIT + sub * F::SUBV, v);
+    F::prep_sub(v, g, sub, rec + u * F::XREC);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // weight streaming: a double-buffered pipeline of load phases
 // ---------------------------------------------------------------------------
@@ -500,15 +514,46 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
     // weights in flight while records are staged; with one load phase they
     // stay in registers, so the next rows of the slot reuse them
     if (Stream<F, H, LPR, 2, C::G>::P > 1 || t0 == 0) st.load(0, mats, rows, I, valid);
-    __syncthreads();
+    // a later row overwrites the records and staging the previous row's
+    // products read; in the fused launch an item's first row follows the
+    // barrier that ended the previous item
+    if (!TAG || t0 > 0) __syncthreads();
     if (STAGE_LOCAL && cached) {
-      if (tid() == 0) {
-        sig_exp[0] = sigma_exp<F>(g_xmax);
-        inv_sigma[0] = __builtin_ldexpf(1.0f, -sig_exp[0]);
-        srcs[0] = lds + S::LDS_BYTES;
+      // sigma from the staged row's maximum, which every thread reads (it was
+      // written before an earlier barrier)
+      const int se = sigma_exp<F>(g_xmax);
+      if (tid() == 0) inv_sigma[0] = __builtin_ldexpf(1.0f, -se);
+      build_row_records<F, H, true, true>(lds + S::LDS_BYTES, se, rec);
+    } else if constexpr (STAGE_LOCAL && TAG) {
+      // the row goes to the staging area and becomes the staged row; every
+      // thread takes sigma from the four waves' maxima
+      uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < XCH; ++i) {
+        const int ch = tid() + i * kThreads;
+        if (ch < H / 8) {
+          *reinterpret_cast<u32x4*>(xs + 8 * ch) = xq[0][i];
+          const uint32_t w[4] = {xq[0][i].x, xq[0][i].y, xq[0][i].z, xq[0][i].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = (w[q] & 0x7FFFu) << 16, hi = (w[q] >> 16 & 0x7FFFu) << 16;
+            m = m > lo ? m : lo;
+            m = m > hi ? m : hi;
+          }
+        }
       }
+      m = wave_max_u32(m);
+      if ((tid() & 63) == 0) red[tid() >> 6] = m;
       __syncthreads();
-      build_records<F, H, true, true>(srcs, nb, sig_exp, rec, tid(), kThreads);
+      for (int w = 0; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
+      const int se = sigma_exp<F>(m);
+      if (tid() == 0) {
+        inv_sigma[0] = __builtin_ldexpf(1.0f, -se);
+        g_xrow = sl.row[t0];
+        g_xmax = m;
+      }
+      build_row_records<F, H, true, true>(xs, se, rec);
     } else if constexpr (STAGE_LOCAL) {
       uint16_t* xs = reinterpret_cast<uint16_t*>(lds + S::LDS_BYTES);
 #pragma unroll
@@ -616,46 +661,54 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
   for (int t0 = 0; t0 < nt_all; t0 += kNTB) {
     const int nb = nt_all - t0 < kNTB ? nt_all - t0 : kNTB;
     if (Stream<F, I, LPR, NPG, C::G>::P > 1 || t0 == 0) st.load(0, mats, rows, H, valid);   // kept for later rows
-    __syncthreads();
+    if (!TAG || t0 > 0) __syncthreads();   // as in gateup_tile
     bool lost = false;   // a wait for h gave up: this tile's partials are NaN
     if constexpr (TAG) {
       // h comes from gate/up workgroups of the same launch: wait for its
-      // tagged words and stage the values in LDS
+      // tagged words, stage the values in LDS and take the row's largest
+      // |h| from the same registers; every thread then derives sigma from
+      // the four waves' maxima
+      static_assert(kNTB == 1, "one h row at a time");
       float* hs = reinterpret_cast<float*>(lds + S::LDS_BYTES);
       constexpr int PER = (I + kThreads - 1) / kThreads;
-      bool got = true;
-      for (int t = 0; t < nb; ++t) {
-        const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0 + t]) * I;
-        // the whole vector polled at once (a sparse first wait on one word
-        // per gate/up tile cost a round trip more than it saved in polls)
-        uint32_t v[PER];
-        got = await_batch<PER>(
-                  [src](int j) -> const uint64_t* {
-                    const int i = tid() + j * kThreads;
-                    return i < I ? src + i : nullptr;
-                  },
-                  tag, a.err, v, a.spin_limit) && got;
+      const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0]) * I;
+      uint32_t v[PER];
+      const bool got = await_batch<PER>(
+          [src](int j) -> const uint64_t* {
+            const int i = tid() + j * kThreads;
+            return i < I ? src + i : nullptr;
+          },
+          tag, a.err, v, a.spin_limit);
+      uint32_t m = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const int i = tid() + j * kThreads;
-          if (i < I) hs[t * I + i] = __builtin_bit_cast(float, v[j]);
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid() + j * kThreads;
+        if (i < I) {
+          hs[i] = __builtin_bit_cast(float, v[j]);
+          const uint32_t mag = v[j] & 0x7FFFFFFFu;
+          m = m > mag ? m : mag;
         }
       }
-      if (tid() < nb) srcs[tid()] = hs + tid() * I;
+      m = wave_max_u32(m);
+      if ((tid() & 63) == 0) red[tid() >> 6] = m;
       lost = __syncthreads_or(!got);
+      for (int w = 0; w < kThreads / 64; ++w) m = m > red[w] ? m : red[w];
+      const int se = sigma_exp<F>(m);
+      if (tid() == 0) inv_sigma[0] = __builtin_ldexpf(1.0f, -se);
+      build_row_records<F, I, false, true>(hs, se, rec);
     } else {
       if (tid() < nb) srcs[tid()] = a.h + static_cast<size_t>(sl.pair[t0 + tid()]) * I;
-    }
-    __syncthreads();
-    for (int t = 0; t < nb; ++t) {
-      const uint32_t m = row_max_bits<I, false, TAG>(srcs[t], red);
-      if (tid() == 0) {
-        sig_exp[t] = sigma_exp<F>(m);
-        inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
+      __syncthreads();
+      for (int t = 0; t < nb; ++t) {
+        const uint32_t m = row_max_bits<I, false, false>(srcs[t], red);
+        if (tid() == 0) {
+          sig_exp[t] = sigma_exp<F>(m);
+          inv_sigma[t] = __builtin_ldexpf(1.0f, -sig_exp[t]);
+        }
       }
+      __syncthreads();
+      build_records<F, I, false, false>(srcs, nb, sig_exp, rec, tid(), kThreads);
     }
-    __syncthreads();
-    build_records<F, I, false, TAG>(srcs, nb, sig_exp, rec, tid(), kThreads);
     __syncthreads();
     float acc[NPG][kNTB] = {};
     st.template run<kNTB>(mats, rows, H, valid, rec, nb, acc, table);
