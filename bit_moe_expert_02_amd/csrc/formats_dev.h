@@ -406,22 +406,25 @@ struct FmtTern {
 };
 
 // =========================================================================
-// Q3: unit = a quarter block: 64 weights = 4 sub-blocks of 16; 16 bytes of
-// the low plane, 8 bytes of the high plane (words for sub-block pairs), the
-// block's fp16 d and the unit's four 6-bit sub-scales (24 bits of the 96).
-// 3-bit codes q = lo + 4 hi are assembled at p = 3, 5, 7: low fields from
-// lo << 3 (i = 0,1,2), lo >> 3 (i = 3,4,5), lo >> 7 (i = 6,7); high bits from
-// the high word shifted so that hi_i lands at p + 2.
+// Q3: unit = a quarter block: 64 weights = 4 sub-blocks of 16; 24 code bytes
+// (six words), the block's fp16 d and the unit's four 6-bit sub-scales (24
+// bits of the 96).  Pair P = 8j + i of the unit is (weight i, weight i+8) of
+// sub-block j.  Pairs 0..29 are 3-bit fields of word P / 5 at bit 1 + 3f
+// (f = P % 5) of each half: f = 0, 1, 2 are taken in place (p = 1, 4, 7),
+// f = 3, 4 from the word shifted right by 9 (p = 1, 4); one v_and_or_b32 per
+// pair.  Pairs 30 and 31 keep code bit b in bit 0 of each half of word
+// 3(P - 30) + b and are assembled at p = 7.
 // =========================================================================
 struct FmtQ3 {
   static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 256) * 110); }
   static constexpr int TAG = 3;
-  static constexpr int UNIT = 64, XREC = 144, PSHIFT = 7, SUBS = 4, SUBV = 16;
+  static constexpr int UNIT = 64, XREC = 144, PSHIFT = 9, SUBS = 4, SUBV = 16;
   static constexpr int units(int k) { return k / 64; }
-  static constexpr int kP[8] = {3, 5, 7, 3, 5, 7, 5, 7};
+  // p of pair P
+  static constexpr int kP[32] = {1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 1,
+                                 4, 7, 1, 4, 1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 7, 7};
   struct Raw {
-    uint32_t lo[4];
-    uint32_t hi[2];
+    uint32_t c[6];
     uint32_t d;
     uint32_t u24;  // the unit's four 6-bit sub-scales
   };
@@ -430,10 +433,10 @@ struct FmtQ3 {
     const uint32_t ku = static_cast<uint32_t>(b & 3);
     const uint32_t nb = static_cast<uint32_t>(nbu) >> 2;
     const uint32_t blk = static_cast<uint32_t>(n) * nb + static_cast<uint32_t>(b >> 2);
-    const u32x4 l = bload128(m, blk * 96u + 16u * ku);
-    const u32x2 h = bload64(m, blk * 96u + 64u + 8u * ku);
-    r.lo[0] = l.x; r.lo[1] = l.y; r.lo[2] = l.z; r.lo[3] = l.w;
-    r.hi[0] = h.x; r.hi[1] = h.y;
+    const u32x4 l = bload128(m, blk * 96u + 24u * ku);
+    const u32x2 h = bload64(m, blk * 96u + 24u * ku + 16u);
+    r.c[0] = l.x; r.c[1] = l.y; r.c[2] = l.z; r.c[3] = l.w;
+    r.c[4] = h.x; r.c[5] = h.y;
     const uint32_t dplane = static_cast<uint32_t>(nrows) * nb * 96u;
     r.d = bload16(m, dplane + blk * 2u);
     const uint32_t w0 = ku >= 2 ? 1u : 0u;
@@ -443,75 +446,81 @@ struct FmtQ3 {
     const uint64_t pair = static_cast<uint64_t>(u0) | (static_cast<uint64_t>(u1) << 32);
     r.u24 = static_cast<uint32_t>(pair >> (24u * ku - 32u * w0)) & 0xFFFFFFu;
   }
-  // sub-unit j = sub-block j: values 16j .. 16j+15
+  // sub-unit j = sub-block j: values 16j .. 16j+15, pairs 8j .. 8j+7
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int j, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], g, kP[i], 4.0f, s));
+    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], g, kP[8 * j + i], 4.0f, s));
     reinterpret_cast<float*>(rec)[32 + j] = s;
+  }
+  // the f16 pair of pair P from the unit's words (w: the words, ws: w >> 9)
+  __device__ static __forceinline__ uint32_t pair_of(const uint32_t (&w)[6], const uint32_t (&ws)[6],
+                                                     const uint32_t (&sp)[2], int P) {
+    constexpr uint32_t F0 = 0x000E000Eu, F1 = 0x00700070u, F2 = 0x03800380u;
+    if (P >= 30) return sp[P - 30];
+    const int m = P / 5, f = P % 5;
+    return f == 0 ? andor(w[m], F0, kMag)
+         : f == 1 ? andor(w[m], F1, kMag)
+         : f == 2 ? andor(w[m], F2, kMag)
+         : f == 3 ? andor(ws[m], F0, kMag)
+                  : andor(ws[m], F1, kMag);
   }
   template <int RT, int NT>
   __device__ static __forceinline__ void dot(const Raw (&raw)[RT], const uint8_t* xr, int rstride,
                                              int nt, float (&acc)[RT][NT]) {
+    uint32_t ws[RT][6], sp[RT][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int par = j & 1;
-      uint32_t pr[RT][8];
-      // low 2-bit fields at p = 3, 5, 7 and the high bit at p + 2, both halves
-      constexpr uint32_t L3 = 0x00180018u, L5 = 0x00600060u, L7 = 0x01800180u;
-      constexpr uint32_t H3 = 0x00200020u, H5 = 0x00800080u, H7 = 0x02000200u;
+    for (int r = 0; r < RT; ++r) {
 #pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const uint32_t lo = raw[r].lo[j], hw = raw[r].hi[j >> 1];
-        const uint32_t la = lo << 3, lb = lo >> 3, lc = lo >> 7;
-        const uint32_t ha = hw << (5 - par), hb = hw >> (par + 1), hc = hw >> (par + 5);
-        pr[r][0] = andor(ha, H3, andor(la, L3, kMag));
-        pr[r][1] = andor(ha, H5, andor(la, L5, kMag));
-        pr[r][2] = andor(ha, H7, andor(la, L7, kMag));
-        pr[r][3] = andor(hb, H3, andor(lb, L3, kMag));
-        pr[r][4] = andor(hb, H5, andor(lb, L5, kMag));
-        pr[r][5] = andor(hb, H7, andor(lb, L7, kMag));
-        pr[r][6] = andor(hc, H5, andor(lc, L5, kMag));
-        pr[r][7] = andor(hc, H7, andor(lc, L7, kMag));
-      }
-      float bd[RT][NT];
+      for (int m = 0; m < 6; ++m) ws[r][m] = raw[r].c[m] >> 9;
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
+      for (int q = 0; q < 2; ++q)
+        sp[r][q] = andor(raw[r].c[3 * q] << 7, 0x00800080u,
+                         andor(raw[r].c[3 * q + 1] << 8, 0x01000100u,
+                               andor(raw[r].c[3 * q + 2] << 9, 0x02000200u, kMag)));
+    }
+    float bd[RT][NT][4];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bd[r][t] = 0.0f;
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bd[r][t][j] = 0.0f;
+    // four pairs (one 16-byte record read) at a time
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < nt) {
-          const uint4 xa = *reinterpret_cast<const uint4*>(xr + t * rstride + j * 32);
-          const uint4 xb = *reinterpret_cast<const uint4*>(xr + t * rstride + j * 32 + 16);
+          const uint4 xa = *reinterpret_cast<const uint4*>(xr + t * rstride + g * 16);
+          const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
           for (int r = 0; r < RT; ++r) {
-            float a = 0.0f;
-            a = dot2(pr[r][0], xa.x, a);
-            a = dot2(pr[r][1], xa.y, a);
-            a = dot2(pr[r][2], xa.z, a);
-            a = dot2(pr[r][3], xa.w, a);
-            a = dot2(pr[r][4], xb.x, a);
-            a = dot2(pr[r][5], xb.y, a);
-            a = dot2(pr[r][6], xb.z, a);
-            a = dot2(pr[r][7], xb.w, a);
-            bd[r][t] = a;
-          }
-        }
-      }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        if (t < nt) {
-          const float S = *reinterpret_cast<const float*>(xr + t * rstride + 128 + 4 * j);
-#pragma unroll
-          for (int r = 0; r < RT; ++r) {
-            const int sj = static_cast<int>((raw[r].u24 >> (6 * j)) & 63u) - 32;
-            const float ds = f16_bits_to_f32(raw[r].d) * static_cast<float>(sj);
-            acc[r][t] = fmaf(ds, bd[r][t] - S, acc[r][t]);
+            for (int e = 0; e < 4; ++e) {
+              const int P = 4 * g + e;
+              bd[r][t][P / 8] = dot2(pair_of(raw[r].c, ws[r], sp[r], P), xv[e], bd[r][t][P / 8]);
+            }
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t < nt) {
+        const float4 S = *reinterpret_cast<const float4*>(xr + t * rstride + 128);
+        const float Sj[4] = {S.x, S.y, S.z, S.w};
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          const float d = f16_bits_to_f32(raw[r].d);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int sj = static_cast<int>((raw[r].u24 >> (6 * j)) & 63u) - 32;
+            acc[r][t] = fmaf(d * static_cast<float>(sj), bd[r][t][j] - Sj[j], acc[r][t]);
+          }
+        }
+      }
     }
   }
 };

@@ -114,6 +114,19 @@ inline float rintf_even(float v) { return std::nearbyint(v); }   // default mode
 
 inline float div_or_zero(float w, float d) { return d == 0.0f ? 0.0f : w / d; }
 
+// Q3 code bit b of weight i (0..255) of a block, as a bit index into the
+// block's 96 code bytes.  By quarter block u (64 weights, six little-endian
+// words at byte 24u): weight t of the quarter's sub-block j belongs to pair
+// P = 8j + t % 8 and to half h = t / 8.  Pairs 0..29 hold 3-bit fields at bit
+// 16h + 1 + 3(P % 5) of word P / 5; pairs 30 and 31 keep code bit b in bit 16h
+// of word 3(P - 30) + b.
+inline int q3_code_bit(int i, int b) {
+  const int u = i >> 6, w = i & 63, j = w >> 4, t = w & 15, h = t >> 3;
+  const int pair = 8 * j + (t & 7);
+  if (pair < 30) return 192 * u + 32 * (pair / 5) + 16 * h + 1 + 3 * (pair % 5) + b;
+  return 192 * u + 32 * (3 * (pair - 30) + b) + 16 * h;
+}
+
 // element of largest magnitude, sign kept; the first one on ties
 inline float signed_absmax(const float* b, int n) {
   float best = b[0];
@@ -198,10 +211,10 @@ void pack_rows(int fmt, const float* w, int64_t n, int64_t k, uint8_t* dst, int6
             for (int i = 0; i < 16; ++i) {
               float q = rintf_even(div_or_zero(blk[16 * j + i], ds)) + 4.0f;
               const int qi = static_cast<int>(std::min(7.0f, std::max(0.0f, q)));
-              const int wi = 16 * j + i;
-              c[(2 * wi) >> 3] |= static_cast<uint8_t>((qi & 3) << ((2 * wi) & 7));
-              const int hb = 32 * (j >> 1) + 2 * i + (j & 1);
-              c[64 + (hb >> 3)] |= static_cast<uint8_t>(((qi >> 2) & 1) << (hb & 7));
+              for (int b = 0; b < 3; ++b) {
+                const int pos = q3_code_bit(16 * j + i, b);
+                c[pos >> 3] |= static_cast<uint8_t>(((qi >> b) & 1) << (pos & 7));
+              }
             }
           }
           put_f16(scales + bi * 2, dh);
@@ -297,10 +310,12 @@ bool unpack_rows(int fmt, const uint8_t* src, int64_t n, int64_t k, float* out, 
             const float ds = d * static_cast<float>(u - 32);                 // exact: 11 x 6 bits
             for (int i = 0; i < 16; ++i) {
               const int wi = 16 * j + i;
-              const int lo = (c[(2 * wi) >> 3] >> ((2 * wi) & 7)) & 3;
-              const int hb = 32 * (j >> 1) + 2 * i + (j & 1);
-              const int hi = (c[64 + (hb >> 3)] >> (hb & 7)) & 1;
-              v[wi] = ds * static_cast<float>(lo + 4 * hi - 4);               // exact: 17 x 3 bits
+              int q = 0;
+              for (int b = 0; b < 3; ++b) {
+                const int pos = q3_code_bit(wi, b);
+                q |= ((c[pos >> 3] >> (pos & 7)) & 1) << b;
+              }
+              v[wi] = ds * static_cast<float>(q - 4);                         // exact: 17 x 3 bits
             }
           }
           break;

@@ -28,11 +28,14 @@
  *   MOE_FMT_TERN160 160 w/block: 32 bytes, byte j = sum_m (t_{5j+m}+1)*3^m
  *                   (values 243..255 invalid) + fp16 d; value d*t.  Rows whose
  *                   length is not a multiple of 160 are padded with zero trits.
- *   MOE_FMT_Q3      256 w/block, 16 sub-blocks of 16: 64-byte low plane (low 2
- *                   bits of q_i at bits [2i,2i+2)), 32-byte high plane (32-bit
- *                   word m: bit 2i = high bit of weight i of sub-block 2m, bit
- *                   2i+1 = of sub-block 2m+1), fp16 d, 12 bytes of sixteen 6-bit
- *                   u_j at bits [6j,6j+6);  value d*(u_j-32)*(q-4).  3.4375 bpw
+ *   MOE_FMT_Q3      256 w/block, 16 sub-blocks of 16: 96 code bytes of 3-bit
+ *                   q, fp16 d, 12 bytes of sixteen 6-bit u_j at bits
+ *                   [6j,6j+6);  value d*(u_j-32)*(q-4).  3.4375 bpw.  Codes
+ *                   by quarter block (six little-endian words at byte 24u):
+ *                   weight t of the quarter's sub-block j is in pair
+ *                   P = 8j + t%8, half h = t/8; P < 30: the field at bit
+ *                   16h+1+3(P%5) of word P/5; P = 30+s: code bit b is bit 16h
+ *                   of word 3s+b
  *   MOE_FMT_MXFP4   32 w/block: 16 bytes of e2m1 (element i in byte i/2, low
  *                   nibble for even i) + e8m0 E (255 invalid);
  *                   value 2^(E-127)*e2m1 (OCP MX v1.0).                 4.25 bpw

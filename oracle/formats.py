@@ -20,11 +20,14 @@ bit order below are this library's own definitions:
           5j..5j+4 as sum_m (t_{5j+m} + 1) * 3^m (bytes 243..255 invalid);
           value = d * t.  A row whose length is not a multiple of 160 is
           padded with zero trits to the next block.               1.7 bpw
-  Q3      256 weights / block = 16 sub-blocks of 16: 64-byte low plane
-          (weight i's low 2 bits at bits [2i, 2i+2)), 32-byte high plane
-          (32-bit word m covers sub-blocks 2m and 2m+1: weight i of sub-block
-          2m at bit 2i, of sub-block 2m+1 at bit 2i+1), fp16 d, and 12 bytes of
-          sixteen 6-bit sub-scales u_j at bits [6j, 6j+6).  q = lo + 4*hi,
+  Q3      256 weights / block = 16 sub-blocks of 16: 96 code bytes, fp16 d,
+          and 12 bytes of sixteen 6-bit sub-scales u_j at bits [6j, 6j+6).
+          The 3-bit codes q are laid out by quarter block (64 weights, four
+          sub-blocks, 24 bytes = six little-endian 32-bit words W0..W5 at
+          byte 24u).  Weight t of the quarter's sub-block j (t < 8: low
+          half, else high half h = 1) belongs to pair P = 8j + (t mod 8).
+          For P < 30 its code is the 3-bit field at bit 16h + 1 + 3(P mod 5)
+          of W_{P div 5}; for P = 30 + s, code bit b is bit 16h of W_{3s+b}.
           value = d * (u_j - 32) * (q - 4).                    3.4375 bpw
   MXFP4   32 weights / block: 16 code bytes (element i in byte i/2, low nibble
           for even i) + one e8m0 byte E.  value = 2^(E-127) * e2m1(c), with
@@ -205,12 +208,22 @@ def decode_tern160(buf, n, k):
 # ----------------------------------------------------------------------------
 # Q3
 # ----------------------------------------------------------------------------
-def _q3_hi_bit_position(sub, i):
-    """Bit index inside the 256-bit high plane of weight i of sub-block `sub`."""
-    return 32 * (sub // 2) + 2 * i + (sub % 2)
+def _q3_code_bits(i):
+    """The three bit indices (code bit 0, 1, 2) of weight i of a block inside
+    its 768-bit code string."""
+    u, w = divmod(i, 64)
+    j, t = divmod(w, 16)
+    h, kk = divmod(t, 8)
+    pair = 8 * j + kk
+    base = 192 * u
+    if pair < 30:
+        m, f = divmod(pair, 5)
+        return [base + 32 * m + 16 * h + 1 + 3 * f + b for b in range(3)]
+    sp = pair - 30
+    return [base + 32 * (3 * sp + b) + 16 * h for b in range(3)]
 
 
-_Q3_HI_POS = np.array([[_q3_hi_bit_position(j, i) for i in range(16)] for j in range(16)]).reshape(256)
+_Q3_BITS = np.array([_q3_code_bits(i) for i in range(256)])            # [256, 3]
 
 
 def pack_q3(w):
@@ -229,11 +242,10 @@ def pack_q3(w):
     ds = (d.astype(np.float32)[..., None] * s.astype(np.float32)).astype(np.float32)
     q = np.clip(np.rint(_div_or(sub, ds[..., None], 0.0)) + 4, 0, 7).astype(np.uint32)
     q = q.reshape(*blk.shape)
-    lo = _fields_to_bytes(q & 3, 2)                      # [N, nb, 64]
-    hi_bits = np.zeros((*q.shape[:-1], 256), np.uint8)
-    hi_bits[..., _Q3_HI_POS] = (q >> 2) & 1
-    hi = _bits_to_bytes(hi_bits)                          # [N, nb, 32]
-    codes = np.concatenate([lo, hi], axis=-1)             # [N, nb, 96]
+    bits = np.zeros((*q.shape[:-1], 768), np.uint8)
+    for b in range(3):
+        bits[..., _Q3_BITS[:, b]] = (q >> b) & 1
+    codes = _bits_to_bytes(bits)                          # [N, nb, 96]
     d_plane = d.view(np.uint8).reshape(-1)
     u_plane = _fields_to_bytes(u, 6).reshape(-1)          # 12 bytes per block
     return np.concatenate([codes.reshape(-1), d_plane, u_plane])
@@ -243,9 +255,8 @@ def decode_q3(buf, n, k):
     codes, rest, nb = _split(buf, "Q3", n, k)
     d = rest[: n * nb * 2].view("<f2").reshape(n, nb).astype(np.float64)
     u = _bytes_to_fields(rest[n * nb * 2:].reshape(n, nb, 12), 6, 16)    # [N, nb, 16]
-    lo = _bytes_to_fields(codes[..., :64], 2, 256)
-    hi = _bytes_to_bits(codes[..., 64:])[..., _Q3_HI_POS].astype(np.int64)
-    q = lo + 4 * hi                                                       # [N, nb, 256]
+    bits = _bytes_to_bits(codes).astype(np.int64)                         # [N, nb, 768]
+    q = sum(bits[..., _Q3_BITS[:, b]] << b for b in range(3))             # [N, nb, 256]
     s = (u - 32).astype(np.float64)
     val = d[..., None, None] * s[..., None] * (q.reshape(n, nb, 16, 16) - 4.0)
     return val.reshape(n, nb * 256)

@@ -155,19 +155,27 @@ def test_q3_on_grid_layout():
                     q[j, :] = 4
             w[r, 256 * b:256 * b + 256] = (d * s[:, None] * (q - 4)).reshape(256)
             qf = q.reshape(256)
-            lo = bytearray(64)
-            hi = bytearray(32)
+            # the layout rule, word by word: quarter u holds six 32-bit words;
+            # pairs 0..29 are 3-bit fields at 16h + 1 + 3f of word P // 5,
+            # pairs 30 and 31 spread their bits over bit 16h of three words
+            words = [[0] * 6 for _ in range(4)]
             for i in range(256):
-                lo[(2 * i) // 8] |= int(qf[i] & 3) << ((2 * i) % 8)
-                sub, ii = divmod(i, 16)
-                bit = 32 * (sub // 2) + 2 * ii + (sub % 2)
-                hi[bit // 8] |= int(qf[i] >> 2) << (bit % 8)
+                u, rem = divmod(i, 64)
+                j, t = divmod(rem, 16)
+                h, kk = divmod(t, 8)
+                pr = 8 * j + kk
+                if pr < 30:
+                    words[u][pr // 5] |= int(qf[i]) << (16 * h + 1 + 3 * (pr % 5))
+                else:
+                    for bb in range(3):
+                        words[u][3 * (pr - 30) + bb] |= ((int(qf[i]) >> bb) & 1) << (16 * h)
+            code = b"".join(wv.to_bytes(4, "little") for wq in words for wv in wq)
             u = bytearray(12)
             for j in range(16):
                 for bb in range(6):
                     pos = 6 * j + bb
                     u[pos // 8] |= (((int(s[j]) + 32) >> bb) & 1) << (pos % 8)
-            exp_lo.append(bytes(lo) + bytes(hi))
+            exp_lo.append(code)
             exp_d.append(bytes(_fp16_bytes(d)))
             exp_u.append(bytes(u))
     buf = F.pack("Q3", w)
@@ -256,3 +264,38 @@ def test_block_multiple_required():
     with pytest.raises(ValueError):
         F.packed_bytes("Q2_0", 1, 100)
     assert F.packed_bytes("TERN160", 1, 100) == 34
+
+
+def test_q3_layout_hand_worked_bits():
+    """One block whose sub-blocks all have the signed absmax -4 (so s * d is
+    1 to fp16 rounding and q = w + 4): every code is 4 (value 0) except weight
+    0 -> q = 7 (pair 0, low half: bits 1..3 of word 0), weight 8 -> q = 1
+    (pair 0, high half: bits 17..19 of word 0), weight 54 -> q = 3 (quarter 0,
+    sub-block 3, t = 6: pair 30, low half: bit 0 of words 0, 1, 2) and the
+    absmax weights (16 j + 3, and 16 instead of 19) -> q = 0."""
+    q = np.full(256, 4)
+    q[0], q[8], q[54] = 7, 1, 3
+    q[16 * np.arange(16) + 3] = 0      # every sub-block's signed absmax is -4 ...
+    q[19], q[16] = 4, 0                # ... sub-block 1 has it at weight 16
+    w = (q - 4.0).astype(np.float32).reshape(1, 256)
+    buf = F.pack("Q3", w)
+    code = buf[:96]
+    word = [int.from_bytes(code[4 * i:4 * i + 4].tobytes(), "little") for i in range(24)]
+    # pair 0 of quarter 0: weights 0 (low) and 8 (high) at bits 1..3 / 17..19
+    assert (word[0] >> 1) & 7 == 7 and (word[0] >> 17) & 7 == 1
+    # pair 30 of quarter 0 (sub-block 3, t = 6 and 14): weight 54 = 3 = 0b011
+    # -> bit 0 of words 0, 1, 2 = 1, 1, 0; weight 62 = 4 = 0b100 -> bit 16 of
+    # words 0, 1, 2 = 0, 0, 1
+    assert [(word[b] >> 0) & 1 for b in range(3)] == [1, 1, 0]
+    assert [(word[b] >> 16) & 1 for b in range(3)] == [0, 0, 1]
+    # weight 3 (q = 0, pair 3: word 0, field 3 at bits 10..12) and weight 35
+    # (q = 0, sub-block 2, t = 3: pair 19 -> word 3, field 4 at bits 13..15)
+    assert (word[0] >> 10) & 7 == 0 and (word[3] >> 13) & 7 == 0
+    # weight 19 (q = 4, sub-block 1, t = 3: pair 11 -> word 2, bits 4..6)
+    assert (word[2] >> 4) & 7 == 4
+    # a code-4 weight: weight 1 (pair 1: word 0, field 1, bits 4..6)
+    assert (word[0] >> 4) & 7 == 4
+    # d = fp16(1 / 31), every s = 31: the decoded values are d * 31 * (q - 4)
+    ds = float(np.float16(np.float32(1.0) / np.float32(31.0))) * 31.0
+    assert np.array_equal(F.decode("Q3", buf, 1, 256)[0], ds * (q - 4.0))
+
