@@ -408,21 +408,22 @@ struct FmtTern {
 // =========================================================================
 // Q3: unit = a quarter block: 64 weights = 4 sub-blocks of 16; 24 code bytes
 // (six words), the block's fp16 d and the unit's four 6-bit sub-scales (24
-// bits of the 96).  Pair P = 8j + i of the unit is (weight i, weight i+8) of
-// sub-block j.  Pairs 0..29 are 3-bit fields of word P / 5 at bit 1 + 3f
-// (f = P % 5) of each half: f = 0, 1, 2 are taken in place (p = 1, 4, 7),
-// f = 3, 4 from the word shifted right by 9 (p = 1, 4); one v_and_or_b32 per
-// pair.  Pairs 30 and 31 keep code bit b in bit 0 of each half of word
-// 3(P - 30) + b and are assembled at p = 7.
+// bits of the 96).  Pair i of sub-block j is (weight i, weight i+8); its
+// codes are 3-bit fields at the same place in both halves of a word: field f
+// at bit 1 + 3f.  Pairs 0-2 of every sub-block sit in fields 0 / 3 (p = 1),
+// pairs 3-5 in fields 1 / 4 (p = 4), pairs 6-7 in field 2 (p = 7) or, for
+// the last two of the unit, spread over bit 0 of each half of three words
+// (assembled at p = 7).  Fields 0-2 are taken in place, 3-4 from the word
+// shifted right by 9: one v_and_or_b32 per pair, and every pair's p depends
+// only on its index in the sub-block, so records are built with constant
+// scales.
 // =========================================================================
 struct FmtQ3 {
   static constexpr uint32_t bytes(int n, int k) { return static_cast<uint32_t>(n * (k / 256) * 110); }
   static constexpr int TAG = 3;
   static constexpr int UNIT = 64, XREC = 144, PSHIFT = 9, SUBS = 4, SUBV = 16;
   static constexpr int units(int k) { return k / 64; }
-  // p of pair P
-  static constexpr int kP[32] = {1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 1,
-                                 4, 7, 1, 4, 1, 4, 7, 1, 4, 1, 4, 7, 1, 4, 7, 7};
+  static constexpr int kP[8] = {1, 1, 1, 4, 4, 4, 7, 7};
   struct Raw {
     uint32_t c[6];
     uint32_t d;
@@ -446,81 +447,77 @@ struct FmtQ3 {
     const uint64_t pair = static_cast<uint64_t>(u0) | (static_cast<uint64_t>(u1) << 32);
     r.u24 = static_cast<uint32_t>(pair >> (24u * ku - 32u * w0)) & 0xFFFFFFu;
   }
-  // sub-unit j = sub-block j: values 16j .. 16j+15, pairs 8j .. 8j+7
+  // sub-unit j = sub-block j: values 16j .. 16j+15
   __device__ static __forceinline__ void prep_sub(const float (&v)[16], float g, int j, uint8_t* rec) {
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], g, kP[8 * j + i], 4.0f, s));
+    for (int i = 0; i < 8; ++i) rec_store(rec, j * 8 + i, make_pair(v[i], v[i + 8], g, kP[i], 4.0f, s));
     reinterpret_cast<float*>(rec)[32 + j] = s;
   }
-  // the f16 pair of pair P from the unit's words (w: the words, ws: w >> 9)
-  __device__ static __forceinline__ uint32_t pair_of(const uint32_t (&w)[6], const uint32_t (&ws)[6],
-                                                     const uint32_t (&sp)[2], int P) {
+  // the f16 pair of pair i of sub-block j (both compile-time after unrolling)
+  __device__ static __forceinline__ uint32_t pair_of(const uint32_t (&w)[6], const uint32_t (&sp)[2], int j,
+                                                     int i) {
     constexpr uint32_t F0 = 0x000E000Eu, F1 = 0x00700070u, F2 = 0x03800380u;
-    if (P >= 30) return sp[P - 30];
-    const int m = P / 5, f = P % 5;
-    return f == 0 ? andor(w[m], F0, kMag)
-         : f == 1 ? andor(w[m], F1, kMag)
-         : f == 2 ? andor(w[m], F2, kMag)
-         : f == 3 ? andor(ws[m], F0, kMag)
-                  : andor(ws[m], F1, kMag);
+    if (i < 6) {
+      const int q = 3 * j + i % 3, m = q % 6;
+      const uint32_t mask = i < 3 ? F0 : F1;
+      return andor(q < 6 ? w[m] : w[m] >> 9, mask, kMag);
+    }
+    const int q = 2 * j + i - 6;
+    return q < 6 ? andor(w[q], F2, kMag) : sp[q - 6];
   }
   template <int RT, int NT>
   __device__ static __forceinline__ void dot(const Raw (&raw)[RT], const uint8_t* xr, int rstride,
                                              int nt, float (&acc)[RT][NT]) {
-    uint32_t ws[RT][6], sp[RT][2];
+    uint32_t sp[RT][2];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-#pragma unroll
-      for (int m = 0; m < 6; ++m) ws[r][m] = raw[r].c[m] >> 9;
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         sp[r][q] = andor(raw[r].c[3 * q] << 7, 0x00800080u,
                          andor(raw[r].c[3 * q + 1] << 8, 0x01000100u,
                                andor(raw[r].c[3 * q + 2] << 9, 0x02000200u, kMag)));
     }
-    float bd[RT][NT][4];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int j = 0; j < 4; ++j) {
+      float bd[RT][NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bd[r][t][j] = 0.0f;
-    // four pairs (one 16-byte record read) at a time
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
+        for (int t = 0; t < NT; ++t) bd[r][t] = 0.0f;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         if (t < nt) {
-          const uint4 xa = *reinterpret_cast<const uint4*>(xr + t * rstride + g * 16);
-          const uint32_t xv[4] = {xa.x, xa.y, xa.z, xa.w};
+          const uint4 xa = *reinterpret_cast<const uint4*>(xr + t * rstride + j * 32);
+          const uint4 xb = *reinterpret_cast<const uint4*>(xr + t * rstride + j * 32 + 16);
 #pragma unroll
           for (int r = 0; r < RT; ++r) {
+            float a = 0.0f;
+            a = dot2(pair_of(raw[r].c, sp[r], j, 0), xa.x, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 1), xa.y, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 2), xa.z, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 3), xa.w, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 4), xb.x, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 5), xb.y, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 6), xb.z, a);
+            a = dot2(pair_of(raw[r].c, sp[r], j, 7), xb.w, a);
+            bd[r][t] = a;
+          }
+        }
+      }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int P = 4 * g + e;
-              bd[r][t][P / 8] = dot2(pair_of(raw[r].c, ws[r], sp[r], P), xv[e], bd[r][t][P / 8]);
-            }
+      for (int t = 0; t < NT; ++t) {
+        if (t < nt) {
+          const float S = *reinterpret_cast<const float*>(xr + t * rstride + 128 + 4 * j);
+#pragma unroll
+          for (int r = 0; r < RT; ++r) {
+            const int sj = static_cast<int>((raw[r].u24 >> (6 * j)) & 63u) - 32;
+            const float ds = f16_bits_to_f32(raw[r].d) * static_cast<float>(sj);
+            acc[r][t] = fmaf(ds, bd[r][t] - S, acc[r][t]);
           }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t < nt) {
-        const float4 S = *reinterpret_cast<const float4*>(xr + t * rstride + 128);
-        const float Sj[4] = {S.x, S.y, S.z, S.w};
-#pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          const float d = f16_bits_to_f32(raw[r].d);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int sj = static_cast<int>((raw[r].u24 >> (6 * j)) & 63u) - 32;
-            acc[r][t] = fmaf(d * static_cast<float>(sj), bd[r][t][j] - Sj[j], acc[r][t]);
-          }
-        }
-      }
     }
   }
 };

@@ -116,15 +116,20 @@ inline float div_or_zero(float w, float d) { return d == 0.0f ? 0.0f : w / d; }
 
 // Q3 code bit b of weight i (0..255) of a block, as a bit index into the
 // block's 96 code bytes.  By quarter block u (64 weights, six little-endian
-// words at byte 24u): weight t of the quarter's sub-block j belongs to pair
-// P = 8j + t % 8 and to half h = t / 8.  Pairs 0..29 hold 3-bit fields at bit
-// 16h + 1 + 3(P % 5) of word P / 5; pairs 30 and 31 keep code bit b in bit 16h
-// of word 3(P - 30) + b.
+// words at byte 24u): weight t of the quarter's sub-block j is in half
+// h = t / 8 of pair p = t % 8; field f of a word is the 3 bits at 16h + 1 + 3f.
+// Pairs p < 6 go to field p / 3 (+ 3 from the second six on) of word q % 6,
+// q = 3j + p % 3; pairs p >= 6 to field 2 of word q = 2j + p - 6 for q < 6,
+// else code bit b sits in bit 16h of word 3(q - 6) + b.
 inline int q3_code_bit(int i, int b) {
-  const int u = i >> 6, w = i & 63, j = w >> 4, t = w & 15, h = t >> 3;
-  const int pair = 8 * j + (t & 7);
-  if (pair < 30) return 192 * u + 32 * (pair / 5) + 16 * h + 1 + 3 * (pair % 5) + b;
-  return 192 * u + 32 * (3 * (pair - 30) + b) + 16 * h;
+  const int u = i >> 6, w = i & 63, j = w >> 4, t = w & 15, h = t >> 3, p = t & 7;
+  if (p < 6) {
+    const int q = 3 * j + p % 3, f = p / 3 + (q < 6 ? 0 : 3);
+    return 192 * u + 32 * (q % 6) + 16 * h + 1 + 3 * f + b;
+  }
+  const int q = 2 * j + p - 6;
+  if (q < 6) return 192 * u + 32 * q + 16 * h + 1 + 3 * 2 + b;
+  return 192 * u + 32 * (3 * (q - 6) + b) + 16 * h;
 }
 
 // element of largest magnitude, sign kept; the first one on ties

@@ -32,10 +32,11 @@
  *                   q, fp16 d, 12 bytes of sixteen 6-bit u_j at bits
  *                   [6j,6j+6);  value d*(u_j-32)*(q-4).  3.4375 bpw.  Codes
  *                   by quarter block (six little-endian words at byte 24u):
- *                   weight t of the quarter's sub-block j is in pair
- *                   P = 8j + t%8, half h = t/8; P < 30: the field at bit
- *                   16h+1+3(P%5) of word P/5; P = 30+s: code bit b is bit 16h
- *                   of word 3s+b
+ *                   weight t of the quarter's sub-block j is in half h = t/8
+ *                   of pair p = t%8; field f = the 3 bits at 16h+1+3f of a
+ *                   word; p < 6: q = 3j + p%3, field p/3 (+3 if q >= 6) of
+ *                   word q%6; p >= 6: q = 2j + p-6, field 2 of word q (q < 6),
+ *                   else code bit b is bit 16h of word 3(q-6)+b
  *   MOE_FMT_MXFP4   32 w/block: 16 bytes of e2m1 (element i in byte i/2, low
  *                   nibble for even i) + e8m0 E (255 invalid);
  *                   value 2^(E-127)*e2m1 (OCP MX v1.0).                 4.25 bpw

@@ -24,10 +24,12 @@ bit order below are this library's own definitions:
           and 12 bytes of sixteen 6-bit sub-scales u_j at bits [6j, 6j+6).
           The 3-bit codes q are laid out by quarter block (64 weights, four
           sub-blocks, 24 bytes = six little-endian 32-bit words W0..W5 at
-          byte 24u).  Weight t of the quarter's sub-block j (t < 8: low
-          half, else high half h = 1) belongs to pair P = 8j + (t mod 8).
-          For P < 30 its code is the 3-bit field at bit 16h + 1 + 3(P mod 5)
-          of W_{P div 5}; for P = 30 + s, code bit b is bit 16h of W_{3s+b}.
+          byte 24u).  Weight t of the quarter's sub-block j lies in half
+          h = t div 8 of pair i = t mod 8.  Field f of a word is the 3 bits
+          at 16h + 1 + 3f.  Pairs i < 3: q' = 3j + i, field 0 (q' < 6) or 3
+          of word q' mod 6; pairs 3 <= i < 6: q' = 3j + i - 3, field 1 or 4
+          likewise; pairs i >= 6: q' = 2j + i - 6, field 2 of word q' for
+          q' < 6, else code bit b is bit 16h of word 3(q' - 6) + b.
           value = d * (u_j - 32) * (q - 4).                    3.4375 bpw
   MXFP4   32 weights / block: 16 code bytes (element i in byte i/2, low nibble
           for even i) + one e8m0 byte E.  value = 2^(E-127) * e2m1(c), with
@@ -213,14 +215,17 @@ def _q3_code_bits(i):
     its 768-bit code string."""
     u, w = divmod(i, 64)
     j, t = divmod(w, 16)
-    h, kk = divmod(t, 8)
-    pair = 8 * j + kk
+    h, pr = divmod(t, 8)
     base = 192 * u
-    if pair < 30:
-        m, f = divmod(pair, 5)
-        return [base + 32 * m + 16 * h + 1 + 3 * f + b for b in range(3)]
-    sp = pair - 30
-    return [base + 32 * (3 * sp + b) + 16 * h for b in range(3)]
+    if pr < 6:
+        q = 3 * j + pr % 3
+        m, f = q % 6, (pr // 3) + (0 if q < 6 else 3)
+    else:
+        q = 2 * j + pr - 6
+        if q >= 6:
+            return [base + 32 * (3 * (q - 6) + b) + 16 * h for b in range(3)]
+        m, f = q, 2
+    return [base + 32 * m + 16 * h + 1 + 3 * f + b for b in range(3)]
 
 
 _Q3_BITS = np.array([_q3_code_bits(i) for i in range(256)])            # [256, 3]

@@ -156,19 +156,27 @@ def test_q3_on_grid_layout():
             w[r, 256 * b:256 * b + 256] = (d * s[:, None] * (q - 4)).reshape(256)
             qf = q.reshape(256)
             # the layout rule, word by word: quarter u holds six 32-bit words;
-            # pairs 0..29 are 3-bit fields at 16h + 1 + 3f of word P // 5,
-            # pairs 30 and 31 spread their bits over bit 16h of three words
+            # field f of a word is the 3 bits at 16h + 1 + 3f; pairs 0-2 of
+            # every sub-block fill fields 0 then 3 of the words in turn, pairs
+            # 3-5 fields 1 then 4, pairs 6-7 field 2, the last two spread
+            # their bits over bit 16h of three words
             words = [[0] * 6 for _ in range(4)]
             for i in range(256):
                 u, rem = divmod(i, 64)
                 j, t = divmod(rem, 16)
-                h, kk = divmod(t, 8)
-                pr = 8 * j + kk
-                if pr < 30:
-                    words[u][pr // 5] |= int(qf[i]) << (16 * h + 1 + 3 * (pr % 5))
+                h, pp = divmod(t, 8)
+                if pp < 3 or 3 <= pp < 6:
+                    cls = 0 if pp < 3 else 1
+                    q2 = 3 * j + pp - 3 * cls
+                    word, fld = (q2, cls) if q2 < 6 else (q2 - 6, cls + 3)
+                    words[u][word] |= int(qf[i]) << (16 * h + 1 + 3 * fld)
                 else:
-                    for bb in range(3):
-                        words[u][3 * (pr - 30) + bb] |= ((int(qf[i]) >> bb) & 1) << (16 * h)
+                    q2 = 2 * j + pp - 6
+                    if q2 < 6:
+                        words[u][q2] |= int(qf[i]) << (16 * h + 1 + 3 * 2)
+                    else:
+                        for bb in range(3):
+                            words[u][3 * (q2 - 6) + bb] |= ((int(qf[i]) >> bb) & 1) << (16 * h)
             code = b"".join(wv.to_bytes(4, "little") for wq in words for wv in wq)
             u = bytearray(12)
             for j in range(16):
@@ -269,9 +277,9 @@ def test_block_multiple_required():
 def test_q3_layout_hand_worked_bits():
     """One block whose sub-blocks all have the signed absmax -4 (so s * d is
     1 to fp16 rounding and q = w + 4): every code is 4 (value 0) except weight
-    0 -> q = 7 (pair 0, low half: bits 1..3 of word 0), weight 8 -> q = 1
-    (pair 0, high half: bits 17..19 of word 0), weight 54 -> q = 3 (quarter 0,
-    sub-block 3, t = 6: pair 30, low half: bit 0 of words 0, 1, 2) and the
+    0 -> q = 7 (sub-block 0, pair 0, low half: field 0 of word 0, bits 1..3),
+    weight 8 -> q = 1 (the same pair's high half: bits 17..19), weight 54 ->
+    q = 3 (sub-block 3, pair 6: q' = 6, so bit 0 of words 0, 1, 2) and the
     absmax weights (16 j + 3, and 16 instead of 19) -> q = 0."""
     q = np.full(256, 4)
     q[0], q[8], q[54] = 7, 1, 3
@@ -281,20 +289,21 @@ def test_q3_layout_hand_worked_bits():
     buf = F.pack("Q3", w)
     code = buf[:96]
     word = [int.from_bytes(code[4 * i:4 * i + 4].tobytes(), "little") for i in range(24)]
-    # pair 0 of quarter 0: weights 0 (low) and 8 (high) at bits 1..3 / 17..19
+    # sub-block 0, pair 0: weights 0 (low) and 8 (high) at bits 1..3 / 17..19
     assert (word[0] >> 1) & 7 == 7 and (word[0] >> 17) & 7 == 1
-    # pair 30 of quarter 0 (sub-block 3, t = 6 and 14): weight 54 = 3 = 0b011
-    # -> bit 0 of words 0, 1, 2 = 1, 1, 0; weight 62 = 4 = 0b100 -> bit 16 of
-    # words 0, 1, 2 = 0, 0, 1
+    # sub-block 3, pair 6 (t = 6 and 14): weight 54 = 3 = 0b011 -> bit 0 of
+    # words 0, 1, 2 = 1, 1, 0; weight 62 = 4 = 0b100 -> bit 16 of words 0, 1,
+    # 2 = 0, 0, 1
     assert [(word[b] >> 0) & 1 for b in range(3)] == [1, 1, 0]
     assert [(word[b] >> 16) & 1 for b in range(3)] == [0, 0, 1]
-    # weight 3 (q = 0, pair 3: word 0, field 3 at bits 10..12) and weight 35
-    # (q = 0, sub-block 2, t = 3: pair 19 -> word 3, field 4 at bits 13..15)
-    assert (word[0] >> 10) & 7 == 0 and (word[3] >> 13) & 7 == 0
-    # weight 19 (q = 4, sub-block 1, t = 3: pair 11 -> word 2, bits 4..6)
-    assert (word[2] >> 4) & 7 == 4
-    # a code-4 weight: weight 1 (pair 1: word 0, field 1, bits 4..6)
-    assert (word[0] >> 4) & 7 == 4
+    # weight 3 (q = 0; sub-block 0, pair 3: q' = 0 -> field 1 of word 0, bits
+    # 4..6) and weight 35 (q = 0; sub-block 2, pair 3: q' = 6 -> field 4 of
+    # word 0, bits 13..15)
+    assert (word[0] >> 4) & 7 == 0 and (word[0] >> 13) & 7 == 0
+    # weight 19 (q = 4; sub-block 1, pair 3: q' = 3 -> field 1 of word 3)
+    assert (word[3] >> 4) & 7 == 4
+    # weight 1 (q = 4; sub-block 0, pair 1: q' = 1 -> field 0 of word 1)
+    assert (word[1] >> 1) & 7 == 4
     # d = fp16(1 / 31), every s = 31: the decoded values are d * 31 * (q - 4)
     ds = float(np.float16(np.float32(1.0) / np.float32(31.0))) * 31.0
     assert np.array_equal(F.decode("Q3", buf, 1, 256)[0], ds * (q - 4.0))
