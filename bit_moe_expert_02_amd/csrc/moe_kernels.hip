@@ -196,6 +196,9 @@ struct Shape {
   static constexpr int LDS_SEL_WORDS = kMaxRows * kMaxK * kSelWords * 4;
   static constexpr int LDS_SEL = LDS_SEL_WORDS + kMaxRows * kMaxK * (static_cast<int>(sizeof(moe_expert_ref)) + 8);
   static constexpr int LDS_SEL_OFF = LDS_REC >= LDS_SEL ? 0 : LDS_WITH_STAGE;
+  // the ternary table [LDS_REC, LDS_BYTES) is built once per fused worker:
+  // the selection's staging never overlaps it
+  static_assert(LDS_SEL_OFF + LDS_SEL <= LDS_REC || LDS_SEL_OFF >= LDS_BYTES, "table kept intact");
   // the selection workgroup keeps the whole expert table (up to 64 * kSelQ
   // entries) there
   static constexpr int LDS_REFS = 64 * kSelQ * static_cast<int>(sizeof(moe_expert_ref));
@@ -408,9 +411,13 @@ struct Stream {
   }
 };
 
-template <class F>
+// The ternary decode table (byte -> five trits) in LDS.  The split kernels
+// build it per ternary tile; the fused launch's workers build it once, at
+// their start (no other use of the fused launch's LDS overlaps it), so an
+// item's weight loads are not held back by it.
+template <class F, bool TAG>
 __device__ __forceinline__ void build_tern_table(uint32_t* table) {
-  if constexpr (std::is_same_v<F, FmtTern>)
+  if constexpr (std::is_same_v<F, FmtTern> && !TAG)
     for (int i = tid(); i < 256; i += kThreads) table[i] = FmtTern::table_entry(i);
 }
 
@@ -477,7 +484,7 @@ __device__ __forceinline__ void gateup_tile(const Args& a, const SlotEntry& sl, 
   __shared__ int sig_exp[kNTB];
   __shared__ uint32_t red[16];
   __shared__ const void* srcs[kNTB];
-  build_tern_table<F>(table);
+  build_tern_table<F, TAG>(table);
   const int rg = tid() / LPR, c = tid() % LPR;
   const int n = tile * C::TN + rg;
   const bool valid = n < I;
@@ -644,7 +651,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
   __shared__ int sig_exp[kNTB];
   __shared__ uint32_t red[16];
   __shared__ const void* srcs[kNTB];
-  build_tern_table<F>(table);
+  build_tern_table<F, TAG>(table);
   const int rg = tid() / LPR, c = tid() % LPR;
   const int n0 = tile * C::TN + rg * NPG;
   const Buf md = make_buf(a.weights + sl.ref.down, F::bytes(H, I));
@@ -1509,6 +1516,8 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   __shared__ moe_expert_ref shref;
   __shared__ SlotEntry sl;
   if (tid() == 0 && a.shared) shref = *a.shared;
+  for (int i = tid(); i < 256; i += kThreads)
+    reinterpret_cast<uint32_t*>(lds + S::LDS_REC)[i] = FmtTern::table_entry(i);
   stage_x_row<S>(a, 0, lds);   // before any wait: every gate/up item of row 0 finds x here
 
   const int nsh = a.shared ? uniform(tiles_of<S, true>(shref.fmt)) : 0;
