@@ -8,6 +8,8 @@
         each scaled by what the same counter reads for a device copy of M MiB
         (the run's largest copy dispatch); records a hash of the kernel sources so
         a reader can tell whether the numbers still describe the code.
+    python -m bit_moe_expert_02_amd.profile_summary counters DB OUT.md --kernel NAME --title T --command C
+        per-dispatch medians of every counter of a --pmc run for dispatches of NAME
 
 Reads the rocpd SQLite views that rocprofv3 writes (kernels, counters_collection).
 """
@@ -56,6 +58,38 @@ def traffic(fetch_db, write_db, kernel, calib_mib):
                 write_factor=calib / 1024 / w_ref)
 
 
+def counters_md(db, kernel, title, command):
+    """Median over the dispatches of `kernel` of each counter in a --pmc run,
+    with the wave-cycle shares the SQ counters give."""
+    c = sqlite3.connect(db)
+    cols = [r[1] for r in c.execute("pragma table_info(counters_collection)").fetchall()]
+    name_col = "counter_name" if "counter_name" in cols else "name"
+    rows = c.execute(f"select dispatch_id, kernel_name, {name_col}, value from counters_collection").fetchall()
+    per = {}
+    for _, k, n, v in rows:
+        if kernel in k.split("(")[0]:
+            per.setdefault(n, []).append(v)
+    if not per:
+        raise SystemExit(f"no dispatch of {kernel} in {db}")
+    med = {n: statistics.median(v) for n, v in per.items()}
+    lines = [f"# {title}", "", "Command (repository root on the MI355X):", "", "```", command, "```", "",
+             f"Per-dispatch medians over {max(len(v) for v in per.values())} dispatches of `{kernel}`.", "",
+             "| counter | median per dispatch |", "|---|---|"]
+    for n in sorted(med):
+        lines.append(f"| `{n}` | {med[n]:.6g} |")
+    wc = med.get("SQ_WAVE_CYCLES")
+    if wc:
+        lines += ["", "| share of wave cycles | |", "|---|---|"]
+        for n, what in (("SQ_WAIT_ANY", "waiting (memory, dependencies, barriers)"),
+                        ("SQ_WAIT_INST_ANY", "waiting to issue"),
+                        ("SQ_ACTIVE_INST_ANY", "issuing"),
+                        ("SQ_ACTIVE_INST_VALU", "issuing VALU"),
+                        ("SQ_ACTIVE_INST_LDS", "issuing LDS")):
+            if n in med:
+                lines.append(f"| {what} (`{n}`) | {100 * med[n] / wc:.1f} % |")
+    return "\n".join(lines) + "\n"
+
+
 def trace_md(db, title, command):
     c = sqlite3.connect(db)
     rows = c.execute("select name, count(*), avg(end-start), min(end-start), max(end-start), "
@@ -87,7 +121,17 @@ def main(argv=None):
     q.add_argument("--calib-mib", type=int, required=True)
     q.add_argument("--command-fetch", required=True)
     q.add_argument("--command-write", required=True)
+    k = sub.add_parser("counters")
+    k.add_argument("db")
+    k.add_argument("out")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--title", required=True)
+    k.add_argument("--command", required=True)
     a = p.parse_args(argv)
+    if a.what == "counters":
+        with open(a.out, "w") as f:
+            f.write(counters_md(a.db, a.kernel, a.title, a.command))
+        return 0
     if a.what == "trace":
         with open(a.out, "w") as f:
             f.write(trace_md(a.db, a.title, a.command))
