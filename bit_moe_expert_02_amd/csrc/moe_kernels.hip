@@ -677,6 +677,8 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
       // the four waves' maxima
       static_assert(kNTB == 1, "one h row at a time");
       float* hs = reinterpret_cast<float*>(lds + S::LDS_BYTES);
+      // h overwrites the staged x row: a later gate/up item stages x again
+      if (tid() == 0) g_xrow = -1;
       constexpr int PER = (I + kThreads - 1) / kThreads;
       const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0]) * I;
       uint32_t v[PER];
@@ -1594,17 +1596,30 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
   __syncthreads();
   const int ns = uniform(tab.n_slots);
   const int n_gu = uniform(tab.n_gu), n_dn = uniform(tab.n_dn);
-  // the down list is taken from the shared expert's tiles on (they are the
-  // list's last, from n_dn - sh_dn): its h is ready long before the routed
-  // ones, so its weights stream while the routed gate/up items are still
-  // finishing; the routed slots follow in list order
+  // At one row the down list is taken from the shared expert's tiles on
+  // (they are the list's last, from n_dn - sh_dn): its h is ready long
+  // before the routed ones, so its weights stream while the routed gate/up
+  // items are still finishing; the routed slots follow in list order.
   const int sh_dn = a.shared ? uniform(tab.dn_off[ns] - tab.dn_off[ns - 1]) : 0;
-  // the routed list starts at worker nsw: the workers holding shared tiles
+  // The routed list starts at worker nsw: the workers holding shared tiles
   // get its later positions, so the routed gate/up items start on free
-  // workers as soon as the selection is out
-  for (int j = (w - nsw + nw) % nw; j < n_gu + n_dn; j += nw) {
-    if (j < n_gu) run_item_fused<S, 2>(a, tab, tab.gu_off, ns, j, lds, tag);
-    else run_item_fused<S, 0>(a, tab, tab.dn_off, ns, (j - n_gu + n_dn - sh_dn) % n_dn, lds, tag);
+  // workers as soon as the selection is out.
+  //
+  // With several rows the shared expert's down tiles go to the shared
+  // workers first (its h comes from their own gate/up tiles, done by then):
+  // worker w < nsw takes shared down tiles w, w + nsw, ... before its list
+  // positions, and the list holds only the routed down items.
+  const int pre = (a.R > 1 && w < nsw && w < sh_dn) ? (sh_dn - 1 - w) / nsw + 1 : 0;
+  const int n_list = a.R > 1 ? n_gu + n_dn - sh_dn : n_gu + n_dn;
+  const int dn_first = a.R > 1 ? 0 : n_dn - sh_dn;
+  const int j0 = (w - nsw + nw) % nw;
+  for (int q = 0;; ++q) {
+    const int j = q < pre ? -1 : j0 + (q - pre) * nw;
+    if (j >= n_list) break;
+    const bool gu = j >= 0 && j < n_gu;
+    const int item = gu ? j : j < 0 ? n_dn - sh_dn + w + q * nsw : (j - n_gu + dn_first) % n_dn;
+    if (gu) run_item_fused<S, 2>(a, tab, tab.gu_off, ns, item, lds, tag);
+    else run_item_fused<S, 0>(a, tab, tab.dn_off, ns, item, lds, tag);
   }
 }
 

@@ -321,11 +321,15 @@ def test_expert_ffn_each_format_real_shape(fmt):
     assert np.all(err <= G.REL_L2_TOL)
 
 
-def test_fused_layer_matches_split_calls_real_shape():
+@pytest.mark.parametrize("rows", [2, 5])
+def test_fused_layer_matches_split_calls_real_shape(rows):
     """moe_layer (fused launch) against moe_route + moe_expert_ffn (one launch
-    per step) on the mixed-format verify layer with 5 rows: same ids, same y."""
+    per step) on the mixed-format verify layer: same ids, same y.  With
+    several rows the shared workers run the shared expert's down tiles before
+    their routed items; a down tile overwrites the staged x row, so a later
+    gate/up item of that row must stage x again (the last row came out NaN
+    when it did not)."""
     wl = synth.WORKLOADS["mixed_verify"]
-    rows = 5
     xbits = synth.x_bf16(wl, 0, rows, 21)
     x, idx, w, logits, gap = G.oracle_route(wl, 0, xbits)
     need = sorted(set(idx.reshape(-1).tolist()))
@@ -341,6 +345,7 @@ def test_fused_layer_matches_split_calls_real_shape():
     torch.cuda.synchronize()
     assert np.array_equal(idx2.cpu().numpy(), gi)
     assert np.array_equal(wts2.cpu().numpy(), gw)
+    assert not np.isnan(gy).any(), f"NaN rows of the fused y: {sorted(set(np.where(np.isnan(gy))[0]))}"
     np.testing.assert_allclose(y2.cpu().numpy(), gy, rtol=1e-6, atol=1e-6)
     G.check_routing(gi, gw, idx, w, gap, logits)
 
