@@ -650,6 +650,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
   __shared__ float inv_sigma[kNTB];
   __shared__ int sig_exp[kNTB];
   __shared__ uint32_t red[16];
+  __shared__ float wrow;                 // fused launch: the row's mixing weight
   __shared__ const void* srcs[kNTB];
   build_tern_table<F, TAG>(table);
   const int rg = tid() / LPR, c = tid() % LPR;
@@ -681,13 +682,20 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
       if (tid() == 0) g_xrow = -1;
       constexpr int PER = (I + kThreads - 1) / kThreads;
       const uint64_t* src = a.ht + static_cast<size_t>(sl.pair[t0]) * I;
-      uint32_t v[PER];
-      const bool got = await_batch<PER>(
-          [src](int j) -> const uint64_t* {
+      // a routed pair's mixing weight is published by the selection after
+      // its ids: thread 0 polls it beside its share of h
+      const uint64_t* wsrc = sl.expert >= 0 ? a.selt + (blockIdx.x % kSelRep) * kSelRepWords +
+                                                  static_cast<size_t>(sl.pair[t0]) * kSelWords + 1
+                                            : nullptr;
+      uint32_t v[PER + 1];
+      const bool got = await_batch<PER + 1>(
+          [src, wsrc](int j) -> const uint64_t* {
+            if (j == PER) return tid() == 0 ? wsrc : nullptr;
             const int i = tid() + j * kThreads;
             return i < I ? src + i : nullptr;
           },
           tag, a.err, v, a.spin_limit);
+      if (tid() == 0) wrow = wsrc ? __builtin_bit_cast(float, v[PER]) : sl.w[t0];
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
@@ -729,7 +737,7 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
 #pragma unroll
       for (int t = 0; t < kNTB; ++t) {
         if (t < nb) {
-          const float sc = lost ? __builtin_nanf("") : inv_sigma[t] * sl.w[t0 + t];
+          const float sc = lost ? __builtin_nanf("") : inv_sigma[t] * (TAG ? wrow : sl.w[t0 + t]);
 #pragma unroll
           for (int q = 0; q < NPG; ++q) {
             const size_t o = static_cast<size_t>(sl.pair[t0 + t]) * H + n0 + q;
@@ -1166,6 +1174,20 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
     for (int q = 0; q < kSelQ; ++q) kh[q] = (q == wq && lane == owner) ? 0u : kh[q];   // taken
     my_id = lane == j ? owner + 64 * wq : my_id;
   }
+  // fused launch: entry j of the row is 8 words (id | fmt << 16, weight
+  // bits, then the 32-bit halves of its gate, up and down offsets); lane L
+  // writes word L & 7 of entry L >> 3 into every copy.  Everything but the
+  // weight goes out now: the gate/up items need only ids and offsets, and
+  // the weight (below, after the softmax) is read by the down items.
+  const int nw_sel = a.k * kSelWords, ent = lane >> 3, fld = lane & 7;
+  const int id_e = __shfl(my_id, ent, 64);
+  uint64_t* sel_o = a.selt ? a.selt + static_cast<size_t>(r) * nw_sel + lane : nullptr;
+  if (a.selt && lane < nw_sel && fld != 1) {
+    const uint32_t* f = reinterpret_cast<const uint32_t*>(refs + id_e);   // fmt, reserved, gate, up, down
+    const uint32_t v = fld == 0 ? (static_cast<uint32_t>(id_e) | (f[0] << 16)) : f[fld];
+#pragma unroll
+    for (int c = 0; c < kSelRep; ++c) tstore(sel_o + c * kSelRepWords, tag, v);
+  }
   // the unbiased logit of each lane's selection, fetched from the lane that
   // holds it, then the softmax over the selection: one exp per lane, the max
   // and the sum gathered from the k lanes
@@ -1202,18 +1224,10 @@ __device__ __forceinline__ void select_core(const Args& a, int r, const double (
     a.wts[r * a.k + lane] = w;
   }
   if (a.selt) {
-    // fused launch: entry j of the row is 8 words (id | fmt << 16, weight
-    // bits, then the 32-bit halves of its gate, up and down offsets); lane L
-    // writes word L & 7 of entry L >> 3 into every copy
-    const int nw = a.k * kSelWords, ent = lane >> 3, fld = lane & 7;
-    const int id_e = __shfl(my_id, ent, 64);
     const uint32_t w_e = __shfl(__builtin_bit_cast(uint32_t, w), ent, 64);
-    if (lane < nw) {
-      const uint32_t* f = reinterpret_cast<const uint32_t*>(refs + id_e);   // fmt, reserved, gate, up, down
-      const uint32_t v = fld == 0 ? (static_cast<uint32_t>(id_e) | (f[0] << 16)) : fld == 1 ? w_e : f[fld];
-      uint64_t* o = a.selt + static_cast<size_t>(r) * nw + lane;
+    if (lane < nw_sel && fld == 1) {
 #pragma unroll
-      for (int c = 0; c < kSelRep; ++c) tstore(o + c * kSelRepWords, tag, v);
+      for (int c = 0; c < kSelRep; ++c) tstore(sel_o + c * kSelRepWords, tag, w_e);
     }
   }
 }
@@ -1566,7 +1580,7 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     const bool got = await_batch<PER>(
         [selt = a.selt + (bid % kSelRep) * kSelRepWords, lim = n * kSelWords, lane](int j) -> const uint64_t* {
           const int i = lane + j * 64;
-          return i < lim ? selt + i : nullptr;
+          return i < lim && (i & (kSelWords - 1)) != 1 ? selt + i : nullptr;   // weights come later
         },
         tag, a.err, v, a.spin_limit);
     // a wait that gave up leaves stale words, whose offsets could lie outside
