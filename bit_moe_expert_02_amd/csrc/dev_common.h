@@ -206,6 +206,63 @@ __device__ __forceinline__ bool await_batch(AddrF addr, uint32_t tag, uint32_t* 
   return all;
 }
 
+// await_batch with two polls in flight, for waits whose wave has nothing
+// else in flight (twice the registers): the second set of loads is issued
+// while the first is out, and each set is issued again as soon as it has been
+// checked, so a word is seen about half a round trip sooner.  Every word's
+// address must be valid; the words wanted are the bits of `need`.  The loads
+// are issued by the whole wave without branches and the loop ends when no
+// lane of the wave waits any more, so the compiler counts the loads in flight
+// instead of waiting for all of them.
+template <int N>
+__device__ __forceinline__ void take_ready(const uint64_t (&w)[N], uint32_t tag, uint32_t& done,
+                                           uint32_t (&out)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const bool now = !(done >> j & 1u) && static_cast<uint32_t>(w[j] >> 32) == tag;
+    out[j] = now ? static_cast<uint32_t>(w[j]) : out[j];
+    done |= now ? 1u << j : 0u;
+  }
+}
+
+template <int N, class AddrF>
+__device__ __forceinline__ bool await_batch2(AddrF addr, uint32_t need, uint32_t tag, uint32_t* err,
+                                             uint32_t (&out)[N], int limit) {
+  static_assert(N < 32, "one bit per word");
+  constexpr uint32_t kAll = (1u << N) - 1u;
+  uint64_t wa[N], wb[N];
+  uint32_t done = ~need & kAll;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    wa[j] = tload(addr(j));
+    out[j] = 0;
+  }
+  // each set is issued again when it returns, so the two stay as far apart
+  // as they start: about half a round trip under load (~1.3 us)
+  __builtin_amdgcn_s_sleep(48);
+#pragma unroll
+  for (int j = 0; j < N; ++j) wb[j] = tload(addr(j));
+  // both sets are issued again on every pass, and a pass that found the
+  // words in the second set ends at the top of the next one, before it waits
+  // for anything: no set changes registers on the way round
+  bool all = false;
+  for (int it = 0;; it += 2) {
+    if (all) break;
+    take_ready<N>(wa, tag, done, out);
+    all = __builtin_amdgcn_ballot_w64(done != kAll) == 0;
+    if (all || it >= limit) break;
+#pragma unroll
+    for (int j = 0; j < N; ++j) wa[j] = tload(addr(j));
+    __builtin_amdgcn_sched_barrier(0);   // the first set is out before the second is waited for
+    take_ready<N>(wb, tag, done, out);
+    all = __builtin_amdgcn_ballot_w64(done != kAll) == 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) wb[j] = tload(addr(j));
+  }
+  if (!all) __hip_atomic_store(err, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return done == kAll;
+}
+
 // Payload of *p once it carries `tag`.  After `limit` polls the wait ends,
 // *err is set to `tag` and 0 is returned: a launch always drains, and the
 // failure is recorded for that call in the error word.

@@ -1395,18 +1395,27 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
   if (i >= a.R * S::kH) return;   // whole workgroups: the grid covers R * H exactly
   const int r = i / S::kH, n = i - r * S::kH;
   const int k = a.k;
-  uint32_t w[2 * kMaxK + 1];
-  const bool got = await_batch<2 * kMaxK + 1>(
-      [sel = a.selt, part = a.part_t, r, n, k, sh = a.shared != nullptr, R = a.R](int j) -> const uint64_t* {
-        if (j < kMaxK) return j < k ? sel + kSelWords * (r * k + j) : nullptr;
-        const int q = j - kMaxK;
+  // the pairs' ids (published long before), then the partials and the shared
+  // expert's partial with two polls in flight; partial words a call does not
+  // use read the first id word and are not waited for
+  uint32_t wid[kMaxK], wp[kMaxK + 1];
+  const bool got_id = await_batch<kMaxK>(
+      [sel = a.selt, r, k](int j) -> const uint64_t* { return j < k ? sel + kSelWords * (r * k + j) : nullptr; },
+      tag, a.err, wid, a.spin_limit);
+  const bool has_sh = a.shared != nullptr;
+  uint32_t need = has_sh ? 1u << kMaxK : 0u;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) need |= j < k ? 1u << j : 0u;
+  const bool got_p = await_batch2<kMaxK + 1>(
+      [sel = a.selt, part = a.part_t, r, n, k, sh = has_sh, R = a.R](int q) -> const uint64_t* {
         if (q < k) return part + static_cast<size_t>(r * k + q) * S::kH + n;
-        return (q == kMaxK && sh) ? part + static_cast<size_t>(R * k + r) * S::kH + n : nullptr;
+        return (q == kMaxK && sh) ? part + static_cast<size_t>(R * k + r) * S::kH + n : sel;
       },
-      tag, a.err, w, a.spin_limit);
+      need, tag, a.err, wp, a.spin_limit);
+  const bool got = got_id && got_p;
   int id[kMaxK], rank[kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) id[j] = j < k ? static_cast<int>(w[j] & 0xFFFFu) : 0x7fffffff;
+  for (int j = 0; j < kMaxK; ++j) id[j] = j < k ? static_cast<int>(wid[j] & 0xFFFFu) : 0x7fffffff;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     rank[j] = 0;
@@ -1418,10 +1427,10 @@ __device__ __forceinline__ void combine_out(const Args& a, int i, uint32_t tag) 
   for (int pos = 0; pos < kMaxK; ++pos) {
     float t = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxK; ++j) t = rank[j] == pos ? __builtin_bit_cast(float, w[kMaxK + j]) : t;
+    for (int j = 0; j < kMaxK; ++j) t = rank[j] == pos ? __builtin_bit_cast(float, wp[j]) : t;
     if (pos < k) s += t;
   }
-  if (a.shared) s += __builtin_bit_cast(float, w[2 * kMaxK]);
+  if (a.shared) s += __builtin_bit_cast(float, wp[kMaxK]);
   if (!got || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) s = __builtin_nanf("");
   a.y[i] = s;
   if (!a.x_next) return;
@@ -1577,12 +1586,27 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     constexpr int PER = kSelEntryWords / 64;
     const int lane = tid();
     uint32_t v[PER];
-    const bool got = await_batch<PER>(
-        [selt = a.selt + (bid % kSelRep) * kSelRepWords, lim = n * kSelWords, lane](int j) -> const uint64_t* {
-          const int i = lane + j * 64;
-          return i < lim && (i & (kSelWords - 1)) != 1 ? selt + i : nullptr;   // weights come later
-        },
-        tag, a.err, v, a.spin_limit);
+    const uint64_t* selt = a.selt + (bid % kSelRep) * kSelRepWords;
+    const int lim = n * kSelWords;
+    bool got;
+    if (lim <= 64) {
+      // one word a lane (a row's whole selection): two polls in flight
+      static_assert(kSelEntryWords >= 64, "every lane's word lies in the entry area");
+      uint32_t v1[1];
+      got = await_batch2<1>([selt, lane](int) { return selt + lane; },
+                            lane < lim && (lane & (kSelWords - 1)) != 1 ? 1u : 0u,   // weights come later
+                            tag, a.err, v1, a.spin_limit);
+      v[0] = v1[0];
+#pragma unroll
+      for (int j = 1; j < PER; ++j) v[j] = 0;
+    } else {
+      got = await_batch<PER>(
+          [selt, lim, lane](int j) -> const uint64_t* {
+            const int i = lane + j * 64;
+            return i < lim && (i & (kSelWords - 1)) != 1 ? selt + i : nullptr;   // weights come later
+          },
+          tag, a.err, v, a.spin_limit);
+    }
     // a wait that gave up leaves stale words, whose offsets could lie outside
     // this call's weights: every entry then names expert 0 with weight NaN,
     // so nothing below reads through them and every partial it makes is NaN
