@@ -67,6 +67,8 @@ def parse():
                    help="offload_fp4: device expert slots (default: one layer's worth)")
     p.add_argument("--offload-share", type=float, default=-1.0,
                    help="offload_fp4: share of misses copied; negative: measured (moe_copy_share)")
+    p.add_argument("--stack-rows", default="",
+                   help="stack workloads: row counts to time (default: the workload's own)")
     p.add_argument("--copy-calib-mb", type=int, default=0,
                    help="run one device copy of this many MiB first (a known-size reference "
                         "for hardware byte counters)")
@@ -556,7 +558,8 @@ def bench_stack(args, torch, L, LY, synth):
     layers = build_stack(args, torch, LY, synth, wl)
     hev = HipEvents()
     out_rows = {}
-    for rows in [r for r in wl.rows if r <= 8]:
+    row_counts = [int(r) for r in args.stack_rows.split(",")] if args.stack_rows else wl.rows
+    for rows in [r for r in row_counts if 1 <= r <= 8]:
         noise = np.stack([synth.noise(wl, l, rows) for l in range(wl.layers)])
         ms, b, u, _ = stack_passes(args, torch, L, LY, synth, hev, wl, layers, rows,
                                    lambda i: synth.x_bf16(wl, 0, rows, 50_000 + i), noise)
