@@ -646,6 +646,69 @@ __global__ __launch_bounds__(kThreads) void k_combine(Args a) {
   a.y[i] = bad ? __builtin_nanf("") : s;
 }
 
+// k_combine with four consecutive outputs per thread: 16-byte loads of the
+// partials, issued before the ids are known (a pair marked -1 or invalid
+// still has its slot in the partials; its value is dropped afterwards), and
+// each output summed in the same order as k_combine, so y is bitwise the
+// same.  Used when R * H is a multiple of 4 and y is 16-byte aligned.
+template <int H>
+__global__ __launch_bounds__(kThreads) void k_combine4(Args a) {
+  static_assert(H % 4 == 0, "whole float4 groups per row");
+  const int i = (blockIdx.x * kThreads + threadIdx.x) * 4;
+  if (i >= a.R * H) return;
+  const int r = i / H, n = i - r * H;
+  const int k = a.k;
+  int id[MOE_MAX_TOP_K], rank[MOE_MAX_TOP_K];
+  float4 v[MOE_MAX_TOP_K];
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_TOP_K; ++q)
+    v[q] = q < k ? *reinterpret_cast<const float4*>(a.part + static_cast<size_t>(r * k + q) * H + n)
+                 : float4{0.f, 0.f, 0.f, 0.f};
+  const float4 sh = a.has_shared ? *reinterpret_cast<const float4*>(a.part + static_cast<size_t>(a.R * k + r) * H + n)
+                                 : float4{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_TOP_K; ++q) {
+    id[q] = q < k ? a.idx[r * k + q] : 0x7fffffff;
+    bad = bad || (q < k && (id[q] < -1 || id[q] >= a.E));
+  }
+#pragma unroll
+  for (int q = 0; q < MOE_MAX_TOP_K; ++q) {
+    rank[q] = 0;
+#pragma unroll
+    for (int p = 0; p < MOE_MAX_TOP_K; ++p) rank[q] += id[p] < id[q];
+  }
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pos = 0; pos < MOE_MAX_TOP_K; ++pos) {
+    float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_TOP_K; ++q) {
+      const bool take = rank[q] == pos && id[q] >= 0;
+      const bool here = rank[q] == pos;
+      t[0] = here ? (take ? v[q].x : 0.f) : t[0];
+      t[1] = here ? (take ? v[q].y : 0.f) : t[1];
+      t[2] = here ? (take ? v[q].z : 0.f) : t[2];
+      t[3] = here ? (take ? v[q].w : 0.f) : t[3];
+    }
+    if (pos < k) {
+      s[0] += t[0];
+      s[1] += t[1];
+      s[2] += t[2];
+      s[3] += t[3];
+    }
+  }
+  if (a.has_shared) {
+    s[0] += sh.x;
+    s[1] += sh.y;
+    s[2] += sh.z;
+    s[3] += sh.w;
+  }
+  const float nan = __builtin_nanf("");
+  *reinterpret_cast<float4*>(a.y + i) =
+      bad ? float4{nan, nan, nan, nan} : float4{s[0], s[1], s[2], s[3]};
+}
+
 }  // namespace pf
 
 // ===========================================================================
@@ -672,8 +735,12 @@ int launch_prefill(const moe_dims* d, int rows, pf::Args a, const lay::ManyRowLa
     hipLaunchKernelGGL((pf::k_down<H, I>), dim3(chunk_groups * pf::kXcd * (H / pf::kDnCh)),
                        dim3(pf::kThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(pf::k_combine<H>, dim3((rows * H + pf::kThreads - 1) / pf::kThreads),
-                     dim3(pf::kThreads), 0, s, a);
+  if (reinterpret_cast<uintptr_t>(a.y) % 16 == 0)
+    hipLaunchKernelGGL(pf::k_combine4<H>, dim3((rows * H / 4 + pf::kThreads - 1) / pf::kThreads),
+                       dim3(pf::kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(pf::k_combine<H>, dim3((rows * H + pf::kThreads - 1) / pf::kThreads),
+                       dim3(pf::kThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EDEVICE;
 }
 
