@@ -67,14 +67,22 @@ def test_quant_mxfp8_bit_exact():
     np.testing.assert_array_equal(got, want)
 
 
-def _prefill(dl, xbits, idx, w, rows, flags=L.MOE_ACT_MXFP8, shared=None):
+def _prefill(dl, xbits, idx, w, rows, flags=L.MOE_ACT_MXFP8, shared=None, misaligned=False):
+    """y of a many-row call; with `misaligned`, y starts 4 bytes past a
+    16-byte boundary (the combine then writes one float per thread), and the
+    float before it must stay untouched."""
     wl = dl.wl
     d = L.dims(wl.hidden, wl.inter, wl.n_experts, wl.top_k, flags)
     ws = LY.workspace(d, rows)
-    y = torch.zeros((rows, dl.wl.hidden), dtype=torch.float32, device="cuda")
+    n = rows * dl.wl.hidden
+    flat = torch.zeros(n + 2, dtype=torch.float32, device="cuda")
+    y = flat[1:n + 1].view(rows, dl.wl.hidden) if misaligned else flat[:n].view(rows, dl.wl.hidden)
     L.moe_expert_ffn(d, G.device_inputs(dl.wl, 0, xbits), rows, torch.from_numpy(idx).cuda(),
                      torch.from_numpy(w).cuda(), dl.weights, dl.experts, shared, y, ws)
     torch.cuda.synchronize()
+    if misaligned:
+        assert y.data_ptr() % 16 == 4
+        assert flat[0].item() == 0.0 and flat[n + 1].item() == 0.0   # nothing written outside y
     return y.cpu().numpy()
 
 
@@ -96,6 +104,8 @@ def test_tiny_prefill_every_row():
     _say("max rel L2", f"{err.max():.2e}")
     assert np.all(err <= G.REL_L2_TOL)
     assert np.array_equal(y, _prefill(dl, xbits, idx, w, R))      # bitwise reproducible
+    # a y that is not 16-byte aligned takes the one-wide combine: same bits
+    assert np.array_equal(y, _prefill(dl, xbits, idx, w, R, misaligned=True))
 
 
 def test_real_shape_prefill_sampled_rows():
