@@ -695,7 +695,10 @@ __device__ __forceinline__ void down_tile(const Args& a, const SlotEntry& sl, in
             return i < I ? src + i : nullptr;
           },
           tag, a.err, v, a.spin_limit);
-      if (tid() == 0) wrow = wsrc ? __builtin_bit_cast(float, v[PER]) : sl.w[t0];
+      // a routed entry's own weight is 0 (its word is not read with the
+      // selection) or NaN (the worker's wait for the selection gave up):
+      // adding it keeps the polled weight exact or poisons it
+      if (tid() == 0) wrow = wsrc ? __builtin_bit_cast(float, v[PER]) + sl.w[t0] : sl.w[t0];
       uint32_t m = 0;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
