@@ -1591,9 +1591,9 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
     uint32_t v[PER];
     const uint64_t* selt = a.selt + (bid % kSelRep) * kSelRepWords;
     const int lim = n * kSelWords;
-    bool got;
+    bool got;   // two polls in flight: this wave has nothing else out
     if (lim <= 64) {
-      // one word a lane (a row's whole selection): two polls in flight
+      // one word a lane (a row's whole selection)
       static_assert(kSelEntryWords >= 64, "every lane's word lies in the entry area");
       uint32_t v1[1];
       got = await_batch2<1>([selt, lane](int) { return selt + lane; },
@@ -1603,12 +1603,14 @@ __global__ __launch_bounds__(kThreads, MOE_WAVES_PER_EU) void k_layer(Args a) {
 #pragma unroll
       for (int j = 1; j < PER; ++j) v[j] = 0;
     } else {
-      got = await_batch<PER>(
-          [selt, lim, lane](int j) -> const uint64_t* {
-            const int i = lane + j * 64;
-            return i < lim && (i & (kSelWords - 1)) != 1 ? selt + i : nullptr;   // weights come later
-          },
-          tag, a.err, v, a.spin_limit);
+      uint32_t need = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = lane + j * 64;
+        need |= i < lim && (i & (kSelWords - 1)) != 1 ? 1u << j : 0u;
+      }
+      got = await_batch2<PER>([selt, lane](int j) { return selt + lane + j * 64; }, need, tag, a.err, v,
+                              a.spin_limit);
     }
     // a wait that gave up leaves stale words, whose offsets could lie outside
     // this call's weights: every entry then names expert 0 with weight NaN,
