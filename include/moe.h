@@ -387,7 +387,7 @@ int32_t moe_set_spin_limit(int32_t polls);
 /* The streaming-read ceiling against which the layer's HBM rate is also
  * reported ("DeepSeek-V4.1-Flash served three ways on 4xL20", section 6: the
  * bandwidth a workload sees falls short of the micro-benchmark figure, so a
- * rate is judged against what the device reaches on a plain stream).  Reads the first floor(bytes / 16) 16-byte chunks of `buf` with
+ * rate is compared with what the device reaches on a plain stream).  Reads the first floor(bytes / 16) 16-byte chunks of `buf` with
  * one 16-byte load per lane and `unroll` loads in flight per lane per
  * iteration, grid-striding over `grid` workgroups of 256 threads, and
  * writes one xor checksum per thread to `sink` so that no load is dropped.
